@@ -1,0 +1,57 @@
+"""The oracle's pins must reject plausible mistakes.
+
+Each case plants one mistake in a copy of ``oracle/engram_oracle.c`` (on the
+CPU, in a temporary directory), builds it, and runs the pin suite against
+that build in a subprocess: the suite must fail.  This shows that a dropped
+term, a wrong sign, a transposed operand or a misplaced index anywhere in the
+oracle is caught by something other than the oracle itself.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "engram_oracle.c")
+
+MUTANTS = [
+    ("dx drops the dot term", "dxs[j] = Gs[j] + tx1 - tx2;", "dxs[j] = Gs[j] + tx1;"),
+    ("dk wrong sign", "dks[j] = tk1 - tk2;", "dks[j] = tk1 + tk2;"),
+    ("dk transposed operand", "tk1 = delta * rk * ws[j] * xh", "tk1 = delta * rk * ws[j] * kh"),
+    ("dx missing 1/d", "tx2 = delta * rx * dot * xh / (double)d", "tx2 = delta * rx * dot * xh"),
+    ("dw uses x^ twice", "dws[j] += delta * xh * kh;", "dws[j] += delta * xh * xh;"),
+    ("dz drops (1 - gate)", "dg * gate * (1.0 - gate)", "dg * gate"),
+    ("clamp derivative not blocked", "(fabs(dot) >= c) ? dz / (2.0 * sqrt(fabs(dot))) : 0.0",
+     "dz / (2.0 * sqrt(fabs(dot) > c ? fabs(dot) : c))"),
+    ("eps outside the sqrt", "1.0 / sqrt(sxx / (double)d + eps)", "1.0 / (sqrt(sxx / (double)d) + eps)"),
+    ("rstd without the mean", "1.0 / sqrt(sxx / (double)d + eps)", "1.0 / sqrt(sxx + eps)"),
+    ("sgn(0) taken as +1", "  return 0.0;\n}\n\nstatic double sigmoid", "  return sqrt(c);\n}\n\nstatic double sigmoid"),
+    ("saved rstd fields swapped", "sv[4 * s + 2] = rx;\n    sv[4 * s + 3] = rk;",
+     "sv[4 * s + 2] = rk;\n    sv[4 * s + 3] = rx;"),
+    ("masked token saves the raw gate", "sv[4 * s + 0] = m ? g : 0.0;", "sv[4 * s + 0] = g;"),
+    ("mask ignored in the output", "os[j] = m ? xs[j] + g * v[j] : xs[j];", "os[j] = xs[j] + g * v[j];"),
+    ("value gradient reads stream 0 only", "dv[j] += gate * Gs[j];", "dv[j] += gate * G[j];"),
+    ("value taken from the last key block", "fwd_token(d, x, kv, kv + NS * d, w, m, out, sv, aux);",
+     "fwd_token(d, x, kv, kv + 3 * d, w, m, out, sv, aux);"),
+    ("bf16 rounding half-up instead of ties-to-even", "u += 0x7fffu + ((u >> 16) & 1u);", "u += 0x8000u;"),
+    ("dot over raw (unnormalised) key", "(xs[j] * rx) * ws[j] * (ks[j] * rk)", "(xs[j] * rx) * ws[j] * ks[j]"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_reject_mutant(desc, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                           str(lib), str(mutant), "-lm", "-lpthread"])
+    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
