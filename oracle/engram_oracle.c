@@ -162,8 +162,10 @@ static void fwd_token(int64_t d, const double *x, const double *k, const double 
 /*
  * Backward for one token, from saved state sv (R8) and upstream gradient G.
  *   dx[s*d + j], dk[s*d + j], dv[j] are written; dw[s*d + j] is accumulated.
- *   mdx, mdk, mdv (may be NULL) receive the sum of |terms| of each output
- *   element; mdw (may be NULL) accumulates sum_t |delta x^_j k^_j|.
+ *   mdx, mdk, mdv (may be NULL) receive a magnitude scale of each output
+ *   element: the sum of |terms|, where |delta| is replaced by its bound
+ *   through sum_j |G_j v_j| (dg is a cancelling fp32 sum on the device);
+ *   mdw (may be NULL) accumulates that bound times |x^_j k^_j| over tokens.
  */
 static void bwd_token(int64_t d, const double *x, const double *k, const double *v, const double *w,
                       const double *sv, const double *G, double *dx, double *dk, double *dv,
@@ -178,10 +180,16 @@ static void bwd_token(int64_t d, const double *x, const double *k, const double 
     const double rx = sv[4 * s + 2], rk = sv[4 * s + 3];
     const double *xs = x + (int64_t)s * d, *ks = k + (int64_t)s * d, *ws = w + (int64_t)s * d;
     const double *Gs = G + (int64_t)s * d;
-    double dg = 0.0;
-    for (int64_t j = 0; j < d; ++j) dg += Gs[j] * v[j];
+    double dg = 0.0, dgabs = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      dg += Gs[j] * v[j];
+      dgabs += fabs(Gs[j] * v[j]);
+    }
     const double dz = dg * gate * (1.0 - gate);
     const double delta = (fabs(dot) >= c) ? dz / (2.0 * sqrt(fabs(dot))) : 0.0; /* R2 */
+    /* Magnitude scale of delta for the tolerance outputs: dg is a cancelling
+       sum, so an evaluation of delta is bounded through sum_j |G_j v_j|. */
+    const double dmag = (fabs(dot) >= c) ? dgabs * gate * (1.0 - gate) / (2.0 * sqrt(fabs(dot))) : 0.0;
     double *dxs = dx + (int64_t)s * d, *dks = dk + (int64_t)s * d, *dws = dw + (int64_t)s * d;
     for (int64_t j = 0; j < d; ++j) {
       const double xh = rx * xs[j], kh = rk * ks[j];
@@ -191,10 +199,10 @@ static void bwd_token(int64_t d, const double *x, const double *k, const double 
       dks[j] = tk1 - tk2;
       dws[j] += delta * xh * kh;
       dv[j] += gate * Gs[j]; /* R11: streams summed in order 0..3 */
-      if (mdx) mdx[(int64_t)s * d + j] = fabs(Gs[j]) + fabs(tx1) + fabs(tx2);
-      if (mdk) mdk[(int64_t)s * d + j] = fabs(tk1) + fabs(tk2);
+      if (mdx) mdx[(int64_t)s * d + j] = fabs(Gs[j]) + dmag * rx * (fabs(ws[j] * kh) + fabs(dot * xh) / (double)d);
+      if (mdk) mdk[(int64_t)s * d + j] = dmag * rk * (fabs(ws[j] * xh) + fabs(dot * kh) / (double)d);
       if (mdv) mdv[j] += fabs(gate * Gs[j]);
-      if (mdw) mdw[(int64_t)s * d + j] += fabs(delta * xh * kh);
+      if (mdw) mdw[(int64_t)s * d + j] += dmag * fabs(xh * kh);
     }
   }
 }

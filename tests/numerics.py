@@ -58,8 +58,11 @@ def check_bf16(name, got_bits, ref64, mag, kappa=32.0, extra=None, max_report=5)
         raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} elements outside 1 bf16 ulp: {detail}")
     ref_bits = f32_to_bf16_bits(ref.astype(np.float32))
     exact = np.count_nonzero(np.asarray(got_bits).ravel() == ref_bits)
-    rel_l2 = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
-    return {"n": int(ref.size), "bit_equal_to_rounded_oracle": int(exact), "rel_l2": rel_l2}
+    ref_r = bf16_to_f64(ref_bits)
+    return {"n": int(ref.size), "bit_equal_to_rounded_oracle": int(exact),
+            # squared norms for norm-wise errors (aggregated over chunks by the caller)
+            "sq_diff_rounded": float(np.sum((got - ref_r) ** 2)), "sq_rounded": float(np.sum(ref_r ** 2)),
+            "sq_diff_fp64": float(np.sum((got - ref) ** 2)), "sq_fp64": float(np.sum(ref ** 2))}
 
 
 def check_rel(name, got, ref, rtol, atol=None, max_report=5):
