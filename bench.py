@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the four-stream Engram saved-state gate on one MI355X.
+
+A step is one pass of the whole hot path: engram_gate_fwd then
+engram_gate_bwd over N = 8192 tokens (4 streams x 5120, the backward's
+maximum N), mask Bernoulli(0.9), grad_out N(0,1), synthetic seeded inputs
+already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-large] [--no-cpu]
+
+Also reported: forward-only and backward-only rates at N = 8192 (from HIP
+events around each call inside the timed region), the forward alone at
+N = 1,048,512 tokens in a single launch, and the fp64 CPU oracle's rate on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Engram gate tokens/s + achieved HBM GB/s (% of peak), fwd and fwd+bwd"
+PEAK_GBPS = 8000.0          # MI355X HBM3E
+N_STEP = 8192
+N_LARGE = 1_048_512
+SEED = 0
+P_MASK = 0.9
+FWD_BYTES_PER_TOKEN = 133_185   # X + KV + mask read, out + saved written
+FWD_BYTES_FIXED = 81_920        # weight
+BWD_BYTES_PER_TOKEN = 225_344   # X, KV, saved, grad_out read; grad_x, grad_kv written
+BWD_BYTES_FIXED = 163_840       # weight read, grad_weight written
+
+
+def fwd_bytes(n):
+    return FWD_BYTES_PER_TOKEN * n + FWD_BYTES_FIXED
+
+
+def bwd_bytes(n):
+    return BWD_BYTES_PER_TOKEN * n + BWD_BYTES_FIXED
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE/WRITE_SIZE runs, if
+    they were taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    e = rec.get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def make_inputs(torch, synth, n, dev, grad):
+    import numpy as np
+    x = torch.empty((n, 4, 5120), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((n, 25600), dtype=torch.bfloat16, device=dev)
+    m = torch.empty(n, dtype=torch.uint8, device=dev)
+    synth.dev_normal_bf16(x, SEED, synth.ID_X)
+    synth.dev_normal_bf16(kv, SEED, synth.ID_KV)
+    synth.dev_mask(m, SEED, P_MASK)
+    w = torch.from_numpy(synth.normal_f32(4 * 5120, SEED, synth.ID_W, 1.0, 0.1).reshape(4, 5120)).to(dev)
+    g = None
+    if grad:
+        g = torch.empty((n, 4, 5120), dtype=torch.bfloat16, device=dev)
+        synth.dev_normal_bf16(g, SEED, synth.ID_GRAD)
+    return x, kv, w, m, g
+
+
+def cpu_baseline(seconds=10.0, sample=2048):
+    """The fp64 oracle on the host cores: fwd+bwd over the first `sample`
+    tokens of the same workload, repeated until `seconds` have elapsed."""
+    import oracle
+    import synth
+    inp = synth.host_inputs(sample, seed=SEED, p=P_MASK, grad=True)
+    threads = oracle.default_threads()
+    # one untimed pass touches every page of the outputs
+    oracle.fwd_bf16(inp["x"][:8], inp["kv"][:8], inp["weight"], inp["mask"][:8], threads=threads)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        _, saved = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=threads)
+        oracle.bwd_bf16(inp["x"], inp["kv"], inp["weight"], saved, inp["grad_out"], threads=threads)
+        done += sample
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd on the first {sample} tokens of the N={N_STEP} workload, "
+                      f"repeated {done // sample}x over {el:.1f} s (fp64, {threads} threads)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-large", action="store_true", help="skip the N=1,048,512 forward")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the Engram gate is independent per token, and this "
+              "build has no multi-GPU path (see the sharding notes); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import memory_bound_engram_amd as eg
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = N_STEP
+    x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
+    out = torch.empty_like(x)
+    saved = torch.empty((n, 4, 4), dtype=torch.float32, device=dev)
+    gx = torch.empty_like(x)
+    gkv = torch.empty_like(kv)
+    gw = torch.empty((4, 5120), dtype=torch.float32, device=dev)
+    ws = torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        eg.engram_gate_fwd(x, kv, w, m, out, saved, n, stream=stream)
+        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        eg.engram_gate_fwd(x, kv, w, m, out, saved, n, stream=stream)
+        ev[i][1].record(stream)
+        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n, stream=stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+
+    fwd_gbps = fwd_bytes(n) / (fwd_ms * 1e-3) / 1e9
+    bwd_gbps = bwd_bytes(n) / (bwd_ms * 1e-3) / 1e9
+    both_gbps = (fwd_bytes(n) + bwd_bytes(n)) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
+    dominant = "bwd" if bwd_ms >= fwd_ms else "fwd"
+    if dominant == "bwd":
+        roof = {"kernel": "engram_gate_bwd (main kernel + grad_weight column reduce)",
+                "bound": "hbm", "achieved": round(bwd_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(bwd_gbps / PEAK_GBPS, 4), "launch_us": round(bwd_ms * 1e3, 2),
+                "algorithmic_bytes_per_launch": bwd_bytes(n),
+                "traffic": recorded_traffic("bwd")}
+    else:
+        roof = {"kernel": "engram_fwd_kernel", "bound": "hbm", "achieved": round(fwd_gbps, 1),
+                "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(fwd_gbps / PEAK_GBPS, 4),
+                "launch_us": round(fwd_ms * 1e3, 2), "algorithmic_bytes_per_launch": fwd_bytes(n),
+                "traffic": recorded_traffic("fwd")}
+
+    res = {
+        "metric": METRIC,
+        "value": round(n * K / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "engram gate fwd+bwd, N=8192 tokens x 4 streams x 5120 (bf16 X/KV/grads, "
+                               "fp32 weight/saved), mask Bernoulli(0.9), grad_out N(0,1), seed 0",
+                   "tokens": n, "streams": 4, "hidden": 5120, "mask_p": P_MASK},
+        "fwd": {"tokens_per_s": round(n / (fwd_ms * 1e-3), 1), "us": round(fwd_ms * 1e3, 2),
+                "tensor_gbps": round(fwd_gbps, 1), "frac_of_peak": round(fwd_gbps / PEAK_GBPS, 4)},
+        "bwd": {"tokens_per_s": round(n / (bwd_ms * 1e-3), 1), "us": round(bwd_ms * 1e3, 2),
+                "tensor_gbps": round(bwd_gbps, 1), "frac_of_peak": round(bwd_gbps / PEAK_GBPS, 4)},
+        "fwd_bwd": {"tokens_per_s": round(n / ((fwd_ms + bwd_ms) * 1e-3), 1),
+                    "tensor_gbps": round(both_gbps, 1), "frac_of_peak": round(both_gbps / PEAK_GBPS, 4)},
+        "roofline": roof,
+    }
+    del out, saved, gx, gkv, gw, ws, x, kv, g
+    torch.cuda.empty_cache()
+
+    if not args.no_large:
+        nl = N_LARGE
+        free, _ = torch.cuda.mem_get_info(dev)
+        if free > nl * (2 * 40960 + 51200 + 65) + (2 << 30):
+            xl, kvl, wl, ml, _ = make_inputs(torch, synth, nl, dev, grad=False)
+            outl = torch.empty_like(xl)
+            savl = torch.empty((nl, 4, 4), dtype=torch.float32, device=dev)
+            for _ in range(2):
+                eg.engram_gate_fwd(xl, kvl, wl, ml, outl, savl, nl, stream=stream)
+            reps = 5
+            evl = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+            for i in range(reps):
+                evl[i][0].record(stream)
+                eg.engram_gate_fwd(xl, kvl, wl, ml, outl, savl, nl, stream=stream)
+                evl[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(e[0].elapsed_time(e[1]) for e in evl)[reps // 2]
+            gbps = fwd_bytes(nl) / (ms * 1e-3) / 1e9
+            res["fwd_large"] = {"tokens": nl, "tokens_per_s": round(nl / (ms * 1e-3), 1), "ms": round(ms, 3),
+                                "tensor_gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+            del xl, kvl, outl, savl
+            torch.cuda.empty_cache()
+        else:
+            res["fwd_large"] = {"skipped": f"needs ~{nl * 173 // 1000 // 1000} GB free device memory"}
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * engram.h -- C ABI of libengram: the four-stream Engram saved-state gate,
+ * forward and explicit backward, for AMD Instinct MI355X (gfx950).
+ *
+ * Operation ("Engram saved-state gate", cuDNN frontend documentation,
+ * semantics paragraph).  For token t and stream s (4 streams, d = 5120):
+ *   x = X[t,s,:], k = KV[t, s*d : (s+1)*d], v = KV[t, 4d : 5d], w = weight[s,:]
+ *   rstd_X   = (mean_j x_j^2 + 1e-20)^(-1/2),  rstd_key likewise for k
+ *   dot      = sum_j (x_j rstd_X) w_j (k_j rstd_key)          (fp32)
+ *   gate     = sigmoid( sgn(dot) * sqrt(max(|dot|, 1e-6)) ),   sgn(0) = 0
+ *   out[t,s,j] = mask[t] ? bf16_rne(x_j + gate * v_j) : X[t,s,j]
+ *   saved[t,s,:] = (mask[t] ? gate : 0, dot, rstd_X, rstd_key)
+ * The backward is the gradient of that map for an upstream grad_out G:
+ *   grad_x, grad_kv (keys, then the shared value whose four stream
+ *   contributions are summed in fp32 before one bf16 cast) and grad_weight
+ *   (summed over all tokens).
+ *
+ * Shapes and layout (layout and saved-state paragraphs).  Everything is
+ * dense, row-major and contiguous:
+ *   x, out, grad_out, grad_x : [N][4][5120]  bf16
+ *   kv, grad_kv              : [N][25600]    bf16 (4 keys, then the value)
+ *   weight, grad_weight      : [4][5120]     fp32
+ *   mask                     : [N]           bytes, nonzero = true
+ *   saved                    : [N][4][4]     fp32 (gate, dot, rstd_X, rstd_key)
+ *   workspace                : engram_gate_bwd_workspace_bytes(N) bytes
+ *
+ * Common contract of the compute calls.
+ *   - Every pointer except `stream` is a device pointer on the current HIP
+ *     device; `stream` is a hipStream_t of that device, passed as void*
+ *     (NULL = the null stream).
+ *   - Arguments are validated on the host before any HIP call; a rejected
+ *     call returns a nonzero status and touches neither the device nor the
+ *     stream.  Validation reads no device memory.
+ *   - Accepted calls only enqueue kernels on `stream` and return: no
+ *     allocation, copy, conversion, compilation or synchronisation.  Launch
+ *     errors come back as ENGRAM_ERR_LAUNCH.  Results are ready when the
+ *     stream reaches that point.
+ *   - The caller owns every buffer.  Outputs and the workspace are treated
+ *     as uninitialised on entry and are written in full.  Inputs may alias
+ *     each other; outputs and workspace must not overlap any input or each
+ *     other (saved-state paragraph).
+ *   - The library holds no state between calls and is thread-safe; calls
+ *     on different streams are independent.  Results are bitwise
+ *     reproducible for identical inputs (fixed reduction orders, no atomics).
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every compute entry point returns one of these. */
+typedef enum {
+  ENGRAM_OK = 0,
+  ENGRAM_ERR_NULL = 1,     /* a required pointer is NULL */
+  ENGRAM_ERR_N_RANGE = 2,  /* N outside 1..4194240 (forward) or 1..8192 (backward) */
+  ENGRAM_ERR_N_MULT64 = 3, /* backward N not a multiple of 64 */
+  ENGRAM_ERR_ALIGN = 4,    /* a floating tensor or the workspace is not 16-byte aligned */
+  ENGRAM_ERR_OVERLAP = 5,  /* an output or the workspace overlaps an input or another output */
+  ENGRAM_ERR_LAUNCH = 6    /* the HIP runtime refused the launch (see engram_last_hip_error) */
+} engram_status;
+
+/* Size limits (layout paragraph). */
+#define ENGRAM_STREAMS 4
+#define ENGRAM_HIDDEN 5120
+#define ENGRAM_KV_COLS 25600
+#define ENGRAM_N_MAX 4194240
+#define ENGRAM_BWD_N_MAX 8192
+#define ENGRAM_BWD_N_MULTIPLE 64
+
+/*
+ * Forward ("Engram saved-state gate": semantics, layout and saved-state
+ * paragraphs; argument order of the plan's execute call).
+ *   x      [N][4][5120] bf16, in       16-byte aligned
+ *   kv     [N][25600]   bf16, in       16-byte aligned
+ *   weight [4][5120]    fp32, in       16-byte aligned
+ *   mask   [N]          u8,   in       any alignment
+ *   out    [N][4][5120] bf16, out      16-byte aligned
+ *   saved  [N][4][4]    fp32, out      16-byte aligned
+ *   N      1 <= N <= 4194240
+ * No workspace.  A false mask byte makes out[t] a bit copy of x[t] and saves
+ * gate 0 for every stream of t; dot and both rstd are still saved.
+ */
+engram_status engram_gate_fwd(const void *x, const void *kv, const float *weight, const uint8_t *mask,
+                              void *out, float *saved, int64_t N, void *stream);
+
+/*
+ * Backward ("Engram saved-state gate": layout, saved-state and workspace
+ * paragraphs).
+ *   x, kv, weight  as in the forward, in
+ *   saved  [N][4][4]    fp32, in       the forward's saved for these x/kv/weight
+ *                                      (not verified: the page leaves identity
+ *                                      to the caller)
+ *   grad_out [N][4][5120] bf16, in
+ *   grad_x   [N][4][5120] bf16, out
+ *   grad_kv  [N][25600]   bf16, out    keys' gradients, then the shared value's
+ *   grad_weight [4][5120] fp32, out    overwritten (not accumulated)
+ *   workspace  engram_gate_bwd_workspace_bytes(N) bytes, scratch, 16-byte
+ *              aligned, contents ignored on entry and undefined on exit
+ *   N      64 <= N <= 8192, N % 64 == 0
+ * The mask reaches the backward through saved (gate 0 for a masked token).
+ */
+engram_status engram_gate_bwd(const void *x, const void *kv, const float *weight, const float *saved,
+                              const void *grad_out, void *grad_x, void *grad_kv, float *grad_weight,
+                              void *workspace, int64_t N, void *stream);
+
+/*
+ * Workspace size of the backward in bytes ("Engram saved-state gate",
+ * workspace paragraph): 4 * (16*N + 4*5120*(N/64)), integer division.
+ * Pure host arithmetic; returns 0 for N <= 0.
+ */
+size_t engram_gate_bwd_workspace_bytes(int64_t N);
+
+/* Human-readable name of a status code (static storage). */
+const char *engram_status_string(int status);
+
+/* The hipError_t value behind the last ENGRAM_ERR_LAUNCH on this thread (0 if none). */
+int engram_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

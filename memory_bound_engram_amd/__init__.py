@@ -1,0 +1,134 @@
+"""libengram: the four-stream Engram saved-state gate on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI declared in ``include/engram.h``.  It only
+marshals arguments (device pointers, N, the current stream); every step of
+the computation runs in the HIP kernels of ``libengram.so``.  There is no
+fallback: if the library is missing, importing this package raises.
+
+PyTorch is used only as a source of device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libengram.so")
+
+STREAMS = 4
+HIDDEN = 5120
+KV_COLS = 25600
+N_MAX = 4194240
+BWD_N_MAX = 8192
+BWD_N_MULTIPLE = 64
+
+OK, ERR_NULL, ERR_N_RANGE, ERR_N_MULT64, ERR_ALIGN, ERR_OVERLAP, ERR_LAUNCH = range(7)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libengram.so is not built ({LIB_PATH}); run __graft_entry__.build() "
+                      "or python memory_bound_engram_amd/build.py")
+
+
+def _hip_runtimes():
+    """Paths of every libamdhip64 mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:  # pragma: no cover
+        return []
+
+
+# Streams and device memory come from PyTorch, which ships its own copy of the
+# HIP runtime (same soname as /opt/rocm's).  libengram must bind to that copy:
+# load torch first so the dynamic loader resolves libamdhip64.so.7 to it.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # the C ABI alone (no torch) binds to the system runtime
+    _torch = None
+
+lib = ctypes.CDLL(LIB_PATH)
+if len(_hip_runtimes()) > 1:
+    raise ImportError("two HIP runtimes are loaded in this process " + str(_hip_runtimes()) +
+                      "; libengram would not see torch's streams and memory")
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+lib.engram_gate_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P]
+lib.engram_gate_fwd.restype = ctypes.c_int
+lib.engram_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
+lib.engram_gate_bwd.restype = ctypes.c_int
+lib.engram_gate_bwd_workspace_bytes.argtypes = [_I64]
+lib.engram_gate_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.engram_status_string.argtypes = [ctypes.c_int]
+lib.engram_status_string.restype = ctypes.c_char_p
+lib.engram_last_hip_error.argtypes = []
+lib.engram_last_hip_error.restype = ctypes.c_int
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int):
+        msg = lib.engram_status_string(status).decode()
+        if status == ERR_LAUNCH:
+            msg += f" (hipError {lib.engram_last_hip_error()})"
+        super().__init__(f"libengram status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise EngramError(status)
+
+
+def _ptr(t):
+    """Device address of a tensor (or a raw int address); None stays NULL."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("libengram needs contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    for t in tensors:
+        if t is not None and not isinstance(t, int):
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream().cuda_stream
+
+
+def engram_gate_bwd_workspace_bytes(N: int) -> int:
+    """Backward scratch size in bytes: 4 * (16N + 4*5120*(N//64))."""
+    return int(lib.engram_gate_bwd_workspace_bytes(N))
+
+
+def engram_gate_fwd(x, kv, weight, mask, out, saved, N=None, stream=None) -> None:
+    """Enqueue the forward on `stream` (default: the current torch stream).
+
+    x [N,4,5120] bf16, kv [N,25600] bf16, weight [4,5120] fp32, mask [N]
+    bool/uint8, out [N,4,5120] bf16 (written), saved [N,4,4] fp32 (written).
+    """
+    if N is None:
+        N = x.shape[0]
+    _check(lib.engram_gate_fwd(_ptr(x), _ptr(kv), _ptr(weight), _ptr(mask), _ptr(out), _ptr(saved), N,
+                               _stream(stream, x)))
+
+
+def engram_gate_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace, N=None,
+                    stream=None) -> None:
+    """Enqueue the backward on `stream` (default: the current torch stream).
+
+    grad_x [N,4,5120] bf16, grad_kv [N,25600] bf16 and grad_weight [4,5120]
+    fp32 are written in full; workspace holds
+    engram_gate_bwd_workspace_bytes(N) bytes of scratch.
+    """
+    if N is None:
+        N = x.shape[0]
+    _check(lib.engram_gate_bwd(_ptr(x), _ptr(kv), _ptr(weight), _ptr(saved), _ptr(grad_out), _ptr(grad_x),
+                               _ptr(grad_kv), _ptr(grad_weight), _ptr(workspace), N, _stream(stream, x)))
+
+
+__all__ = ["engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
+           "LIB_PATH"]

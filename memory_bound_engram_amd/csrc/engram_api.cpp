@@ -1,0 +1,125 @@
+// engram_api.cpp -- the C ABI of libengram: argument validation on the host,
+// then kernel launches on the caller's stream.  Nothing here allocates,
+// copies or synchronises.  Limits and rules: "Engram saved-state gate"
+// (cuDNN frontend docs), layout, saved-state and workspace paragraphs.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "engram.h"
+#include "engram_launch.h"
+
+namespace {
+
+constexpr int64_t kXRowBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 2;  // 40960
+constexpr int64_t kKvRowBytes = (int64_t)ENGRAM_KV_COLS * 2;                 // 51200
+constexpr int64_t kWeightBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 4;  // 81920
+constexpr int64_t kSavedRowBytes = (int64_t)ENGRAM_STREAMS * 4 * 4;          // 64
+constexpr int kFwdWorkgroupsPerCu = 1;
+constexpr int kMaxDevices = 64;
+
+thread_local int g_last_hip_error = 0;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Outputs (and scratch) may overlap neither an input nor each other.
+bool any_overlap(const Range* in, int nin, const Range* out, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlaps(out[i], in[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlaps(out[i], out[j])) return true;
+  }
+  return false;
+}
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int v = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_cu_count[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+engram_status launched(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return e == hipSuccess ? ENGRAM_OK : ENGRAM_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t engram_gate_bwd_workspace_bytes(int64_t N) {
+  if (N <= 0) return 0;
+  return (size_t)4 * ((size_t)16 * (size_t)N + (size_t)4 * ENGRAM_HIDDEN * (size_t)(N / 64));
+}
+
+engram_status engram_gate_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
+                              float* saved, int64_t N, void* stream) {
+  if (!x || !kv || !weight || !mask || !out || !saved) return ENGRAM_ERR_NULL;
+  if (N < 1 || N > ENGRAM_N_MAX) return ENGRAM_ERR_N_RANGE;
+  if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(out) || !aligned16(saved))
+    return ENGRAM_ERR_ALIGN;
+  const Range in[] = {range_of(x, N * kXRowBytes), range_of(kv, N * kKvRowBytes), range_of(weight, kWeightBytes),
+                      range_of(mask, N)};
+  const Range outs[] = {range_of(out, N * kXRowBytes), range_of(saved, N * kSavedRowBytes)};
+  if (any_overlap(in, 4, outs, 2)) return ENGRAM_ERR_OVERLAP;
+  int64_t grid = (int64_t)kFwdWorkgroupsPerCu * cu_count();
+  if (grid > N) grid = N;
+  return launched(engram::launch_fwd(x, kv, weight, mask, out, saved, N, (int)grid, (hipStream_t)stream));
+}
+
+engram_status engram_gate_bwd(const void* x, const void* kv, const float* weight, const float* saved,
+                              const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight, void* workspace,
+                              int64_t N, void* stream) {
+  if (!x || !kv || !weight || !saved || !grad_out || !grad_x || !grad_kv || !grad_weight || !workspace)
+    return ENGRAM_ERR_NULL;
+  if (N < 1 || N > ENGRAM_BWD_N_MAX) return ENGRAM_ERR_N_RANGE;
+  if (N % ENGRAM_BWD_N_MULTIPLE != 0) return ENGRAM_ERR_N_MULT64;
+  if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(saved) || !aligned16(grad_out) ||
+      !aligned16(grad_x) || !aligned16(grad_kv) || !aligned16(grad_weight) || !aligned16(workspace))
+    return ENGRAM_ERR_ALIGN;
+  const Range in[] = {range_of(x, N * kXRowBytes), range_of(kv, N * kKvRowBytes), range_of(weight, kWeightBytes),
+                      range_of(saved, N * kSavedRowBytes), range_of(grad_out, N * kXRowBytes)};
+  const Range outs[] = {range_of(grad_x, N * kXRowBytes), range_of(grad_kv, N * kKvRowBytes),
+                        range_of(grad_weight, kWeightBytes),
+                        range_of(workspace, (int64_t)engram_gate_bwd_workspace_bytes(N))};
+  if (any_overlap(in, 5, outs, 4)) return ENGRAM_ERR_OVERLAP;
+  return launched(engram::launch_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace, N,
+                                     (hipStream_t)stream));
+}
+
+const char* engram_status_string(int status) {
+  switch (status) {
+    case ENGRAM_OK: return "ok";
+    case ENGRAM_ERR_NULL: return "a required pointer is NULL";
+    case ENGRAM_ERR_N_RANGE: return "N out of range (forward 1..4194240, backward 64..8192)";
+    case ENGRAM_ERR_N_MULT64: return "backward N must be a multiple of 64";
+    case ENGRAM_ERR_ALIGN: return "floating tensors and workspace must be 16-byte aligned";
+    case ENGRAM_ERR_OVERLAP: return "outputs/workspace overlap an input or each other";
+    case ENGRAM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int engram_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

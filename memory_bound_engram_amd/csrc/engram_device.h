@@ -1,0 +1,74 @@
+// engram_device.h -- device helpers shared by the libengram kernels (gfx950).
+//
+// Storage: bf16 values travel as 16-byte vectors of eight (u32x4); a bf16 is
+// the upper half of a binary32, so widening is exact and takes one shift or
+// mask per value.  Narrowing uses gfx950's v_cvt_pk_bf16_f32 (round to
+// nearest even), which the compiler emits for a float2 -> bf16x2 vector
+// conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace engram {
+
+constexpr int kStreams = 4;
+constexpr int kHidden = 5120;                 // per-stream hidden size d
+constexpr int kKvCols = 5 * kHidden;          // four keys, then the shared value
+constexpr int kValueCol = 4 * kHidden;        // first column of the shared value
+constexpr int kVec = 8;                       // bf16 per 16-byte vector
+constexpr int kRowVecs = kHidden / kVec;      // 640 vectors per row
+constexpr int kTokensPerPartial = 64;         // grad_weight partial granularity
+constexpr float kEps = 1e-20f;                // normalisation epsilon
+constexpr float kClamp = 1e-6f;               // signed-sqrt clamp
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16x2 (lo in bits 15:0), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void store16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+template <int kCtrl, int kRowMask, int kBankMask, bool kBoundCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, kBankMask, kBoundCtrl));
+}
+
+// Sum over the 64 lanes of a wave; the full sum lands in lane 63 (other
+// lanes hold partial sums).  Fixed order, so the result is deterministic.
+//   quad_perm[1,0,3,2], quad_perm[2,3,0,1]  -> sums of 4
+//   row_half_mirror, row_mirror             -> sums of 16 in every lane of a row
+//   row_bcast:15 (rows 1,3), row_bcast:31 (rows 2,3) -> lane 63 holds all 64
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v += dpp<0xB1, 0xF, 0xF, true>(v);
+  v += dpp<0x4E, 0xF, 0xF, true>(v);
+  v += dpp<0x141, 0xF, 0xF, true>(v);
+  v += dpp<0x140, 0xF, 0xF, true>(v);
+  v += dpp<0x142, 0xA, 0xF, false>(v);
+  v += dpp<0x143, 0xC, 0xF, false>(v);
+  return v;
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+}  // namespace engram

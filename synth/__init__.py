@@ -85,6 +85,7 @@ def _d():
     if _dev is None:
         if not os.path.exists(_DEV_LIB):
             raise RuntimeError(f"device generator not built: {_DEV_LIB} (run __graft_entry__.build())")
+        import torch  # noqa: F401  (bind to the HIP runtime torch loaded)
         lib = ctypes.CDLL(_DEV_LIB)
         P, I64, U64, U32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32
         lib.synth_dev_normal_bf16.argtypes = [P, I64, U64, U32, I64, P]

@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/engram.h declares, sizes the workspace by the page's formula, and
+rejects every invalid call on the host before any HIP call (fake device
+addresses are used, so an accepted call would be a bug)."""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import memory_bound_engram_amd as eg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "gate_spec_constants.json")))
+
+XB = 4 * 5120 * 2       # bytes per token of x / out / grad
+KVB = 25600 * 2         # bytes per token of kv
+WB = 4 * 5120 * 4       # weight bytes
+SB = 64                 # saved bytes per token
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(eg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in engram.h but not exported"
+
+
+def test_header_constants_match_the_page():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (ENGRAM_\w+) (\d+)", text))
+    assert int(consts["ENGRAM_STREAMS"]) == GOLDEN["streams"]["value"]
+    assert int(consts["ENGRAM_HIDDEN"]) == GOLDEN["hidden"]["value"]
+    assert int(consts["ENGRAM_KV_COLS"]) == GOLDEN["kv_columns"]["value"]
+    assert int(consts["ENGRAM_N_MAX"]) == GOLDEN["n_max"]["value"]
+    assert int(consts["ENGRAM_BWD_N_MAX"]) == GOLDEN["bwd_n_max"]["value"]
+    assert int(consts["ENGRAM_BWD_N_MULTIPLE"]) == GOLDEN["bwd_n_multiple"]["value"]
+
+
+@pytest.mark.parametrize("n", [0, -5, 1, 63, 64, 100, 4096, 8192, 8256, 1 << 20])
+def test_workspace_formula(n):
+    want = 4 * (16 * n + 4 * 5120 * (n // 64)) if n > 0 else 0
+    assert eg.engram_gate_bwd_workspace_bytes(n) == want
+
+
+def test_workspace_worked_values():
+    assert eg.engram_gate_bwd_workspace_bytes(64) == 86016
+    assert eg.engram_gate_bwd_workspace_bytes(4096) == 5505024
+    assert eg.engram_gate_bwd_workspace_bytes(8192) == 11010048
+
+
+# ---------------- forward validation ----------------
+
+BASE = 1 << 40  # fake, 16-byte-aligned, never dereferenced
+
+
+def fwd_layout(n):
+    x = BASE
+    kv = x + n * XB + 4096
+    w = kv + n * KVB + 4096
+    m = w + WB + 4096
+    out = m + n + 4096 + 16
+    out -= out % 16
+    sv = out + n * XB + 4096
+    return dict(x=x, kv=kv, w=w, m=m, out=out, sv=sv)
+
+
+def call_fwd(a, n):
+    return eg.lib.engram_gate_fwd(a["x"], a["kv"], a["w"], a["m"], a["out"], a["sv"], n, None)
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "m", "out", "sv"])
+def test_fwd_rejects_null(field):
+    a = fwd_layout(8)
+    a[field] = None
+    assert call_fwd(a, 8) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("n", [0, -1, 4194241, 1 << 40])
+def test_fwd_rejects_n_out_of_range(n):
+    assert call_fwd(fwd_layout(8), n) == eg.ERR_N_RANGE
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "out", "sv"])
+def test_fwd_rejects_misaligned(field):
+    a = fwd_layout(8)
+    a[field] += 2
+    assert call_fwd(a, 8) == eg.ERR_ALIGN
+
+
+def test_fwd_mask_may_be_unaligned_but_overlap_is_checked():
+    a = fwd_layout(8)
+    a["out"] = a["x"]  # out aliases x
+    assert call_fwd(a, 8) == eg.ERR_OVERLAP
+    a = fwd_layout(8)
+    a["sv"] = a["out"] + 8 * XB - 16  # saved overlaps the tail of out
+    assert call_fwd(a, 8) == eg.ERR_OVERLAP
+    a = fwd_layout(8)
+    a["out"] = a["m"] - (a["m"] % 16)  # out starts inside the mask bytes
+    assert call_fwd(a, 8) == eg.ERR_OVERLAP
+    a = fwd_layout(8)
+    a["sv"] = a["w"] + WB - 16  # saved overlaps the weight
+    assert call_fwd(a, 8) == eg.ERR_OVERLAP
+
+
+# ---------------- backward validation ----------------
+
+def bwd_layout(n):
+    p = BASE
+    a = {}
+    for name, size in (("x", n * XB), ("kv", n * KVB), ("w", WB), ("sv", n * SB), ("g", n * XB),
+                       ("dx", n * XB), ("dkv", n * KVB), ("dw", WB),
+                       ("ws", max(eg.engram_gate_bwd_workspace_bytes(n), 16))):
+        a[name] = p
+        p += size + 4096
+    return a
+
+
+def call_bwd(a, n):
+    return eg.lib.engram_gate_bwd(a["x"], a["kv"], a["w"], a["sv"], a["g"], a["dx"], a["dkv"], a["dw"],
+                                  a["ws"], n, None)
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "sv", "g", "dx", "dkv", "dw", "ws"])
+def test_bwd_rejects_null(field):
+    a = bwd_layout(64)
+    a[field] = None
+    assert call_bwd(a, 64) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("n,code", [(0, eg.ERR_N_RANGE), (-64, eg.ERR_N_RANGE), (8256, eg.ERR_N_RANGE),
+                                    (100, eg.ERR_N_MULT64), (1, eg.ERR_N_MULT64), (8191, eg.ERR_N_MULT64)])
+def test_bwd_rejects_bad_n(n, code):
+    assert call_bwd(bwd_layout(max(n, 64)), n) == code
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "sv", "g", "dx", "dkv", "dw", "ws"])
+def test_bwd_rejects_misaligned(field):
+    a = bwd_layout(64)
+    a[field] += 8
+    assert call_bwd(a, 64) == eg.ERR_ALIGN
+
+
+@pytest.mark.parametrize("out,other", [("dx", "x"), ("dx", "g"), ("dkv", "kv"), ("dw", "w"), ("ws", "sv"),
+                                       ("dx", "dkv"), ("ws", "dw"), ("dkv", "ws")])
+def test_bwd_rejects_overlap(out, other):
+    a = bwd_layout(64)
+    a[out] = a[other]
+    assert call_bwd(a, 64) == eg.ERR_OVERLAP
+
+
+def test_bwd_inputs_may_alias_each_other():
+    # grad_out aliasing x is legal; with fake addresses the call then fails only
+    # at launch, so check validation alone via an overlap that is still caught.
+    a = bwd_layout(64)
+    a["g"] = a["x"]
+    a["dx"] = a["x"]
+    assert call_bwd(a, 64) == eg.ERR_OVERLAP
+
+
+def test_status_strings():
+    for s in range(7):
+        assert eg.lib.engram_status_string(s)

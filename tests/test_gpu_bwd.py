@@ -1,0 +1,105 @@
+"""Backward parity: libengram on the GPU vs the fp64 oracle.
+
+As in the tile-kernels backward test, the backward is checked on the
+reference forward's saved intermediates: the oracle's fp32 saved is uploaded
+and both sides consume it.  The device-only chain (device forward -> device
+backward) is checked norm-wise against the oracle chain."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _bwd_case(gpu, inp, threads=8):
+    import torch
+    from gpu_util import dev_inputs, f32, run_bwd, to_dev, u16
+    from parity import check_bwd
+    _, saved_ref = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=threads)
+    d = dev_inputs(inp, gpu)
+    gx, gkv, gw = run_bwd(d, to_dev(saved_ref, gpu))
+    torch.cuda.synchronize()
+    st = check_bwd(inp, saved_ref, u16(gx), u16(gkv), f32(gw), threads=threads)
+    return st, saved_ref, u16(gx), u16(gkv), f32(gw)
+
+
+def test_bwd_n64(gpu):
+    inp = synth.host_inputs(64, seed=0, p=0.9, grad=True)
+    st, *_ = _bwd_case(gpu, inp)
+    print(st)
+
+
+@pytest.mark.parametrize("n", [128, 192, 640, 1088])
+def test_bwd_block_counts(gpu, n):
+    """2, 3, 10 and 17 partial rows: uneven chunks in the grad_weight reduction."""
+    inp = synth.host_inputs(n, seed=n, p=0.7, grad=True)
+    _bwd_case(gpu, inp)
+
+
+def test_fwd_bwd_n4096(gpu):
+    """N = 4096, mask 0.9, grad_out N(0,1): forward parity, backward parity on
+    the oracle's saved, and the device-only chain norm-wise."""
+    import torch
+    from gpu_util import dev_inputs, f32, run_bwd, run_fwd, u16
+    from parity import check_bwd_end_to_end, check_fwd
+    inp = synth.host_inputs(4096, seed=0, p=0.9, grad=True)
+    st_b, saved_ref, *_ = _bwd_case(gpu, inp, threads=16)
+    d = dev_inputs(inp, gpu)
+    out, saved = run_fwd(d)
+    gx, gkv, gw = run_bwd(d, saved)
+    torch.cuda.synchronize()
+    st_f = check_fwd(inp, u16(out), f32(saved), threads=16)
+    st_e = check_bwd_end_to_end(inp, f32(saved), u16(gx), u16(gkv), f32(gw), saved_ref, threads=16)
+    print(st_f, st_b, st_e)
+
+
+def test_bwd_n8192_edge_rows(gpu):
+    """N = 8192 (the backward maximum), mask 0.3, eps/clamp/zero rows."""
+    from numerics import bf16_to_f64
+    n = 8192
+    inp = synth.host_inputs(n, seed=0, p=0.3, grad=True, edge=True)
+    st, saved_ref, dx, dkv, dw = _bwd_case(gpu, inp, threads=16)
+    print(st)
+    off = inp["mask"] == 0
+    # masked tokens: dx = G bit for bit, key and value gradients zero
+    assert np.array_equal(dx[off], inp["grad_out"][off])
+    assert np.all(bf16_to_f64(dkv[off]) == 0.0)
+    # clamp rows (|dot| < 1e-6): dx = G and dk = 0 on that stream
+    dots = saved_ref[:, :, 1]
+    t_idx, s_idx = np.nonzero((np.abs(dots) < np.float32(1e-6)) & ~off[:, None])
+    assert t_idx.size > 100
+    for t, s in zip(t_idx[:64], s_idx[:64]):
+        assert np.array_equal(dx[t, s], inp["grad_out"][t, s])
+        assert np.all(bf16_to_f64(dkv[t, s * 5120:(s + 1) * 5120]) == 0.0)
+
+
+def test_fwd_bwd_repeated_1000_bitwise(gpu):
+    """N = 8192 with the edge-row recipe, mask 0.3: 1000 forward+backward
+    launches back to back on one stream; the last results equal the first
+    bit for bit (no state carried through the workspace)."""
+    import torch
+    import memory_bound_engram_amd as eg
+    from gpu_util import alloc_bwd, dev_inputs, poison
+    n = 8192
+    inp = synth.host_inputs(n, seed=0, p=0.3, grad=True, edge=True)
+    d = dev_inputs(inp, gpu)
+    x, kv, w, m, g = d["x"], d["kv"], d["weight"], d["mask"], d["grad_out"]
+
+    def one(out, saved, gx, gkv, gw, ws):
+        eg.engram_gate_fwd(x, kv, w, m, out, saved, n)
+        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n)
+
+    first = [poison(torch.empty_like(x)), poison(torch.empty((n, 4, 4), dtype=torch.float32, device=gpu)),
+             *alloc_bwd(x, kv, n)]
+    one(*first)
+    again = [poison(torch.empty_like(x)), poison(torch.empty((n, 4, 4), dtype=torch.float32, device=gpu)),
+             *alloc_bwd(x, kv, n)]
+    for _ in range(1000):
+        one(*again)
+    torch.cuda.synchronize()
+    for a, b in zip(first[:5], again[:5]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
