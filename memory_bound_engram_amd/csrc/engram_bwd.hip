@@ -13,14 +13,26 @@
 //   dv_j  = sum_s g^_s G_{s,j}              (fp32, streams in order, one bf16 cast)
 //   dw_{s,j} = sum_t a_{t,s} x_j k_j        (= sum_t delta x^_j k^_j)
 //
-// Kernel 1 (main): one workgroup per 64-token block, 640 threads; thread c
-// owns columns [8c, 8c+8) of every row.  Per token it loads G, X and the keys
-// for all four streams plus the shared value (13 16-byte loads per thread),
-// reduces the four dg sums (DPP within a wave, LDS across waves), and writes
-// grad_x and grad_kv.  The grad_weight contribution a x k of its columns is
-// accumulated in VGPRs over the block's 64 tokens and written once, as row b
-// of the fp32 partials [N/64][4][5120] in the workspace.
-// Kernel 2 (reduce): grad_weight[s][j] = sum over b of the partials, in a
+// Kernel 1 (main).  The grad_weight partials come in rows of 64 tokens; row b
+// holds the tokens b + k*NB (k = 0..63, NB = N/64), so the workgroups that
+// run at the same moment touch neighbouring tokens.  Each row is split by
+// stream: workgroup (b, s) owns stream s of row b and writes that quarter of
+// the partial row, so no two workgroups write the same bytes.  The four stream
+// workgroups of a row share blockIdx % 8 (one XCD, one L2) and walk the same
+// tokens in the same order, so the shared value and the grad_out slices they
+// all read are fetched from HBM once (normal loads; streaming hints would
+// evict them before the sibling workgroups arrive).
+// Inside a workgroup: 2 token slots x 2 half-row waves.  Wave (u, h) handles
+// tokens k = u, u + 2, ... of the row and vectors h + 2i (i = 0..4) of the
+// 640 16-byte vectors of a stream row.  The dg partials of the two half-row
+// waves of a token meet in LDS (one barrier per pair of tokens).  grad_value
+// for vector pair i (columns of vectors 2i, 2i+1) is written by the stream-i
+// workgroup for i < 4 and, for i = 4, by the stream (k mod 4) workgroup, so
+// every element is written once and the extra grad_out reads stay balanced.
+// The weight row of stream s sits in LDS.  Each wave accumulates a x k for its
+// vectors over its 32 tokens in VGPRs; the two token slots are added in slot
+// order at the end.
+// Kernel 2 (reduce): grad_weight[s][j] = sum over rows of the partials, in a
 // fixed order (8 contiguous row chunks summed sequentially, then the chunk
 // sums added in chunk order), so the result is bitwise reproducible.
 //
@@ -33,142 +45,169 @@
 
 namespace engram {
 
-constexpr int kBwdThreads = kRowVecs;        // 640
-constexpr int kBwdWaves = kBwdThreads / 64;  // 10
+constexpr int kBwdSlots = 2;                          // token slots per workgroup
+constexpr int kBwdThreads = 64 * 2 * kBwdSlots;       // 2 half-row waves per slot
+constexpr int kBwdVecs = kRowVecs / 128;              // 5 vectors per lane (half a row)
+constexpr int kTokensPerSlot = kTokensPerPartial / kBwdSlots;
 
 __global__ void __launch_bounds__(kBwdThreads)
 engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
                        const float* __restrict__ weight, const float* __restrict__ saved,
                        const uint16_t* __restrict__ gout, uint16_t* __restrict__ dx,
-                       uint16_t* __restrict__ dkv, float* __restrict__ partial) {
-  __shared__ float red[2][kBwdWaves][4];
-  const int c = threadIdx.x;
-  const int wave = c >> 6, lane = c & 63;
-  const int col = c * kVec;
-  const int64_t block = blockIdx.x;
+                       uint16_t* __restrict__ dkv, float* __restrict__ partial, int nb) {
+  __shared__ f32x4 wrow[kHidden / 4];       // weight row of stream s (20 KB)
+  __shared__ f32x4 comb[kHidden / 4];       // token-slot combine (20 KB)
+  __shared__ float red[2][kBwdSlots][2];    // dg partials of the half-row waves
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int u = wave >> 1, h = wave & 1;
+  // XCD-aware: blockIdx = 32 q + 8 s + r  ->  row b = 8 q + r, stream s
+  const int bi = blockIdx.x;
+  const int r = bi & 7, s = (bi >> 3) & 3;
+  const int64_t b = (int64_t)(bi >> 5) * 8 + r;
+  if (b >= nb) return;  // rows are padded to a multiple of 8
 
-  float w[kStreams][kVec];
+  for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads)
+    wrow[j] = reinterpret_cast<const f32x4*>(weight + s * kHidden)[j];
+  float acc[kBwdVecs][kVec];
 #pragma unroll
-  for (int s = 0; s < kStreams; ++s) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(weight + s * kHidden + col);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(weight + s * kHidden + col + 4);
+  for (int v = 0; v < kBwdVecs; ++v)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w[s][e] = a[e];
-      w[s][4 + e] = b[e];
-    }
-  }
-  float acc[kStreams][kVec];
-#pragma unroll
-  for (int s = 0; s < kStreams; ++s)
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) acc[s][e] = 0.f;
+    for (int e = 0; e < kVec; ++e) acc[v][e] = 0.f;
+  __syncthreads();
 
   int buf = 0;
-  for (int i = 0; i < kTokensPerPartial; ++i) {
-    const int64_t t = block * kTokensPerPartial + i;
-    const uint16_t* xt = x + t * (kStreams * kHidden) + col;
-    const uint16_t* kt = kv + t * kKvCols + col;
-    const uint16_t* gt = gout + t * (kStreams * kHidden) + col;
+  for (int jj = 0; jj < kTokensPerSlot; ++jj) {
+    const int k = u + kBwdSlots * jj;          // index of the token within row b
+    const int64_t t = b + (int64_t)k * nb;
+    const uint16_t* gt = gout + t * (kStreams * kHidden);
+    const uint16_t* xs = x + t * (kStreams * kHidden) + s * kHidden;
+    const uint16_t* kt = kv + t * kKvCols;
+    const bool dv_tail = (k & 3) == s;          // this workgroup also writes vector pair 4
 
-    u32x4 gr[kStreams], xr[kStreams], kr[kStreams];
+    u32x4 gr[kBwdVecs], vr[kBwdVecs], xr[kBwdVecs], kr[kBwdVecs], go[2][kStreams];
 #pragma unroll
-    for (int s = 0; s < kStreams; ++s) gr[s] = load16_stream(gt + s * kHidden);
-    const u32x4 vr = load16_stream(kt + kValueCol);
+    for (int v = 0; v < kBwdVecs; ++v) {
+      const int col = (lane + 64 * (h + 2 * v)) * kVec;
+      gr[v] = load16(gt + s * kHidden + col);
+      vr[v] = load16(kt + kValueCol + col);
+      xr[v] = load16_stream(xs + col);
+      kr[v] = load16_stream(kt + s * kHidden + col);
+    }
+    // the other streams' grad_out at this wave's grad_value vectors
 #pragma unroll
-    for (int s = 0; s < kStreams; ++s) {
-      xr[s] = load16_stream(xt + s * kHidden);
-      kr[s] = load16_stream(kt + s * kHidden);
+    for (int m = 0; m < 2; ++m) {
+      if (m == 1 && !dv_tail) continue;
+      const int col = (lane + 64 * (h + 2 * (m == 0 ? s : 4))) * kVec;
+#pragma unroll
+      for (int so = 0; so < kStreams; ++so)
+        if (so != s) go[m][so] = load16(gt + so * kHidden + col);
     }
 
-    float part[kStreams];
+    float p = 0.f;
 #pragma unroll
-    for (int s = 0; s < kStreams; ++s) {
-      float p = 0.f;
+    for (int v = 0; v < kBwdVecs; ++v)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        p = fmaf(bf_lo(gr[s][q]), bf_lo(vr[q]), p);
-        p = fmaf(bf_hi(gr[s][q]), bf_hi(vr[q]), p);
+        p = fmaf(bf_lo(gr[v][q]), bf_lo(vr[v][q]), p);
+        p = fmaf(bf_hi(gr[v][q]), bf_hi(vr[v][q]), p);
       }
-      part[s] = wave_sum_to_lane63(p);
-    }
-    if (lane == 63) {
-#pragma unroll
-      for (int s = 0; s < kStreams; ++s) red[buf][wave][s] = part[s];
-    }
+    p = wave_sum_to_lane63(p);
+    if (lane == 63) red[buf][u][h] = p;
     __syncthreads();
-    float tot = 0.f;
-    if (lane < kStreams) {
-#pragma unroll
-      for (int v = 0; v < kBwdWaves; ++v) tot += red[buf][v][lane];
-    }
-    buf ^= 1;
+    const float dg = red[buf][u][0] + red[buf][u][1];
+    buf ^= 1;  // the next pair writes the other buffer: one barrier per pair suffices
 
     const float* sv = saved + t * (kStreams * 4);
-    float gh[kStreams], ca[kStreams], cb[kStreams], ce[kStreams];
-#pragma unroll
-    for (int s = 0; s < kStreams; ++s) {
-      const float g = sv[4 * s + 0], dot = sv[4 * s + 1];
-      const float rx = sv[4 * s + 2], rk = sv[4 * s + 3];
-      const float dg = read_lane(tot, s);
-      const float dz = dg * g * (1.0f - g);
-      const float ad = fabsf(dot);
-      const float delta = ad >= kClamp ? dz / (2.0f * sqrtf(ad)) : 0.0f;
-      const float dr = delta * rx;
-      gh[s] = g;
-      ca[s] = dr * rk;
-      cb[s] = dr * rx * (dot / (float)kHidden);
-      ce[s] = delta * rk * rk * (dot / (float)kHidden);
-    }
+    const float g = sv[4 * s + 0], dot = sv[4 * s + 1];
+    const float rx = sv[4 * s + 2], rk = sv[4 * s + 3];
+    const float dz = dg * g * (1.0f - g);
+    const float ad = fabsf(dot);
+    const float delta = ad >= kClamp ? dz / (2.0f * sqrtf(ad)) : 0.0f;
+    const float dr = delta * rx;
+    const float ca = dr * rk;
+    const float cb = dr * rx * (dot / (float)kHidden);
+    const float ce = delta * rk * rk * (dot / (float)kHidden);
 
-    uint16_t* dxt = dx + t * (kStreams * kHidden) + col;
-    uint16_t* dkt = dkv + t * kKvCols + col;
-    float dv[kVec];
+    uint16_t* dxs = dx + t * (kStreams * kHidden) + s * kHidden;
+    uint16_t* dkt = dkv + t * kKvCols;
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) dv[e] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kStreams; ++s) {
+    for (int v = 0; v < kBwdVecs; ++v) {
+      const int vec = lane + 64 * (h + 2 * v);
+      const f32x4 w0 = wrow[2 * vec], w1 = wrow[2 * vec + 1];
+      const float wv[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       u32x4 ox, ok;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float gx[2] = {bf_lo(gr[s][q]), bf_hi(gr[s][q])};
-        float xx[2] = {bf_lo(xr[s][q]), bf_hi(xr[s][q])};
-        float kk[2] = {bf_lo(kr[s][q]), bf_hi(kr[s][q])};
         float rdx[2], rdk[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int e = 2 * q + h;
-          const float wk = w[s][e] * kk[h];
-          const float wx = w[s][e] * xx[h];
-          rdx[h] = fmaf(-cb[s], xx[h], fmaf(ca[s], wk, gx[h]));
-          rdk[h] = fmaf(-ce[s], kk[h], ca[s] * wx);
-          acc[s][e] = fmaf(ca[s], xx[h] * kk[h], acc[s][e]);
-          dv[e] = s == 0 ? gh[0] * gx[h] : fmaf(gh[s], gx[h], dv[e]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int e = 2 * q + hh;
+          const float gx = hh ? bf_hi(gr[v][q]) : bf_lo(gr[v][q]);
+          const float xx = hh ? bf_hi(xr[v][q]) : bf_lo(xr[v][q]);
+          const float kk = hh ? bf_hi(kr[v][q]) : bf_lo(kr[v][q]);
+          rdx[hh] = fmaf(-cb, xx, fmaf(ca, wv[e] * kk, gx));
+          rdk[hh] = fmaf(-ce, kk, ca * (wv[e] * xx));
+          acc[v][e] = fmaf(ca, xx * kk, acc[v][e]);
         }
         ox[q] = pack_bf16x2(rdx[0], rdx[1]);
         ok[q] = pack_bf16x2(rdk[0], rdk[1]);
       }
-      store16_stream(dxt + s * kHidden, ox);
-      store16_stream(dkt + s * kHidden, ok);
+      store16_stream(dxs + vec * kVec, ox);
+      store16_stream(dkt + s * kHidden + vec * kVec, ok);
     }
-    u32x4 ov;
+
+    // grad_value = sum over streams (order 0..3) of gate_s G_s, one bf16 cast
+    float gh[kStreams];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ov[q] = pack_bf16x2(dv[2 * q], dv[2 * q + 1]);
-    store16_stream(dkt + kValueCol, ov);
+    for (int so = 0; so < kStreams; ++so) gh[so] = sv[4 * so];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (m == 1 && !dv_tail) continue;
+      const int vec = lane + 64 * (h + 2 * (m == 0 ? s : 4));
+      u32x4 ov;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // this wave's own stream: vector slot s (m == 0) or 4 (m == 1), selected without
+        // dynamic register indexing
+        const uint32_t own = m == 1 ? gr[4][q] : s == 0 ? gr[0][q] : s == 1 ? gr[1][q] : s == 2 ? gr[2][q] : gr[3][q];
+        float d2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float a = 0.f;
+#pragma unroll
+          for (int so = 0; so < kStreams; ++so) {
+            const uint32_t wd = so == s ? own : go[m][so][q];
+            const float gv = hh ? bf_hi(wd) : bf_lo(wd);
+            a = so == 0 ? gh[0] * gv : fmaf(gh[so], gv, a);
+          }
+          d2[hh] = a;
+        }
+        ov[q] = pack_bf16x2(d2[0], d2[1]);
+      }
+      store16_stream(dkt + kValueCol + vec * kVec, ov);
+    }
   }
 
-  float* prow = partial + block * (kStreams * kHidden) + col;
+  // add the token slots in slot order, then write stream s of partial row b
+  for (int uu = 0; uu < kBwdSlots; ++uu) {
+    if (u == uu) {
 #pragma unroll
-  for (int s = 0; s < kStreams; ++s) {
-    f32x4 a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = acc[s][e];
-      b[e] = acc[s][4 + e];
+      for (int v = 0; v < kBwdVecs; ++v) {
+        const int vec = lane + 64 * (h + 2 * v);
+        f32x4 a0 = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+        f32x4 a1 = {acc[v][4], acc[v][5], acc[v][6], acc[v][7]};
+        if (uu > 0) {
+          a0 += comb[2 * vec];
+          a1 += comb[2 * vec + 1];
+        }
+        comb[2 * vec] = a0;
+        comb[2 * vec + 1] = a1;
+      }
     }
-    *reinterpret_cast<f32x4*>(prow + s * kHidden) = a;
-    *reinterpret_cast<f32x4*>(prow + s * kHidden + 4) = b;
+    __syncthreads();
   }
+  f32x4* prow = reinterpret_cast<f32x4*>(partial + b * (kStreams * kHidden) + s * kHidden);
+  for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads) prow[j] = comb[j];
 }
 
 constexpr int kReduceChunks = 8;                         // row chunks per column group
@@ -206,12 +245,13 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
   uint16_t* dkvp = static_cast<uint16_t*>(dkv);
   float* partial = static_cast<float*>(workspace) + 16 * n;
   const int nb = (int)(n / kTokensPerPartial);
-  void* args1[] = {&xp, &kvp, &weight, &saved, &gp, &dxp, &dkvp, &partial};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_main_kernel), dim3(nb),
+  int nbv = nb;
+  void* args1[] = {&xp, &kvp, &weight, &saved, &gp, &dxp, &dkvp, &partial, &nbv};
+  const int grid1 = (nb + 7) / 8 * 8 * kStreams;  // (row, stream) pairs, rows padded to 8
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_main_kernel), dim3(grid1),
                                  dim3(kBwdThreads), args1, 0, stream);
   if (e != hipSuccess) return e;
   const float* cpartial = partial;
-  int nbv = nb;
   void* args2[] = {&cpartial, &dw, &nbv};
   return hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_reduce_kernel),
                          dim3(kReduceCols4 / kReduceGroups), dim3(kReduceThreads), args2, 0, stream);

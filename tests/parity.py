@@ -114,15 +114,38 @@ def check_bwd(inp, saved32, dx16, dkv16, dw32, threads=8, ref=None):
     return st
 
 
-def check_bwd_end_to_end(inp, saved_dev, dx16, dkv16, dw32, saved_ref, threads=8):
+def check_bwd_end_to_end(inp, saved_dev, dx16, dkv16, dw32, fwd_ref, threads=8):
     """Device backward on the device's own saved vs the oracle backward on the
-    oracle's saved: norm-wise only (1/(2 sqrt|dot|) amplifies forward noise on
-    small-dot rows, so elementwise bars do not apply)."""
+    oracle's saved.
+
+    delta = dg g(1-g) / (2 sqrt|dot|) has |d ln(delta) / d dot| <=
+    |1 - 2g| / (2 sqrt|dot|) + 1 / (2 |dot|), so the forward's admissible dot
+    error (1e-5 |dot| + 2^-22 A) can move delta by a large relative amount on
+    rows with |dot| near that noise floor.  grad_x and grad_key are therefore
+    gated norm-wise (<= 2e-3) on rows whose propagated delta error is <= 1e-3;
+    grad_value (which depends on the gates only) on all rows; grad_weight, a
+    sum over all rows, is reported.
+    """
     x, kv, w, g = inp["x"], inp["kv"], inp["weight"], inp["grad_out"]
+    saved_ref, saved64, aux = fwd_ref[1], fwd_ref[3], fwd_ref[4]
     dx_r, dkv_r, dw_r = oracle.bwd_bf16(x, kv, w, saved_ref, g, threads=threads)
-    st = {"e2e_dx_rel_l2": _rel_l2(bf16_to_f64(dx16), bf16_to_f64(dx_r)),
-          "e2e_dkv_rel_l2": _rel_l2(bf16_to_f64(dkv16), bf16_to_f64(dkv_r)),
-          "e2e_dw_rel_l2": _rel_l2(dw32, dw_r)}
-    for k, v in st.items():
-        assert v <= 2e-3, f"{k} = {v:.3e} exceeds 2e-3"
+    n = x.shape[0]
+    dot = np.abs(saved64[..., 1])
+    gate = saved64[..., 0]
+    tol_dot = 1e-5 * dot + 2.0 ** -22 * aux[..., 0]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sens = np.abs(1 - 2 * gate) / (2 * np.sqrt(dot)) + 1 / (2 * dot)
+        rel_delta = np.where(dot > 0, sens * tol_dot, np.inf)
+    ok = rel_delta <= 1e-3                                   # [n, 4]
+    gx, rx_ = bf16_to_f64(dx16), bf16_to_f64(dx_r)
+    gk = bf16_to_f64(dkv16[:, :4 * D]).reshape(n, 4, D)
+    rk_ = bf16_to_f64(dkv_r[:, :4 * D]).reshape(n, 4, D)
+    st = {"e2e_rows_excluded": int((~ok).sum()),
+          "e2e_dx_rel_l2": _rel_l2(gx[ok], rx_[ok]),
+          "e2e_dk_rel_l2": _rel_l2(gk[ok], rk_[ok]),
+          "e2e_dv_rel_l2": _rel_l2(bf16_to_f64(dkv16[:, 4 * D:]), bf16_to_f64(dkv_r[:, 4 * D:])),
+          "e2e_dx_rel_l2_all_rows": _rel_l2(gx, rx_),
+          "e2e_dw_rel_l2_reported": _rel_l2(dw32, dw_r)}
+    for k in ("e2e_dx_rel_l2", "e2e_dk_rel_l2", "e2e_dv_rel_l2"):
+        assert st[k] <= 2e-3, f"{k} = {st[k]:.3e} exceeds 2e-3"
     return st

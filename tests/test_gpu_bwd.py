@@ -52,8 +52,9 @@ def test_fwd_bwd_n4096(gpu):
     out, saved = run_fwd(d)
     gx, gkv, gw = run_bwd(d, saved)
     torch.cuda.synchronize()
-    st_f = check_fwd(inp, u16(out), f32(saved), threads=16)
-    st_e = check_bwd_end_to_end(inp, f32(saved), u16(gx), u16(gkv), f32(gw), saved_ref, threads=16)
+    fwd_ref = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=16, extras=True)
+    st_f = check_fwd(inp, u16(out), f32(saved), ref=fwd_ref)
+    st_e = check_bwd_end_to_end(inp, f32(saved), u16(gx), u16(gkv), f32(gw), fwd_ref, threads=16)
     print(st_f, st_b, st_e)
 
 
