@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--no-large", action="store_true", help="skip the N=1,048,512 forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the Engram gate is independent per token, and this "
@@ -126,6 +129,14 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     n = N_STEP
     x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
     out = torch.empty_like(x)
