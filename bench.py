@@ -6,7 +6,10 @@ engram_gate_bwd over N = 8192 tokens (4 streams x 5120, the backward's
 maximum N), mask Bernoulli(0.9), grad_out N(0,1), synthetic seeded inputs
 already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-large] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-large] [--no-cpu]
+
+Consecutive steps use R (default 4) independent sets of inputs and outputs,
+so no step finds its data in the 256 MB cache from the previous one.
 
 Also reported: forward-only and backward-only rates at N = 8192 (from HIP
 events around each call inside the timed region), the forward alone at
@@ -114,6 +117,9 @@ def main():
     ap.add_argument("--no-large", action="store_true", help="skip the N=1,048,512 forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="independent input/output sets cycled step by step, so that no step "
+                         "finds its data in cache from the previous one")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -138,21 +144,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     n = N_STEP
-    x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
-    out = torch.empty_like(x)
-    saved = torch.empty((n, 4, 4), dtype=torch.float32, device=dev)
-    gx = torch.empty_like(x)
-    gkv = torch.empty_like(kv)
-    gw = torch.empty((4, 5120), dtype=torch.float32, device=dev)
-    ws = torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    R = max(1, args.rotate)
+    sets = []
+    for _ in range(R):  # same seeded data, distinct memory
+        x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
+        sets.append(dict(x=x, kv=kv, w=w, m=m, g=g, out=torch.empty_like(x),
+                         saved=torch.empty((n, 4, 4), dtype=torch.float32, device=dev),
+                         gx=torch.empty_like(x), gkv=torch.empty_like(kv),
+                         gw=torch.empty((4, 5120), dtype=torch.float32, device=dev),
+                         ws=torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev)))
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        eg.engram_gate_fwd(x, kv, w, m, out, saved, n, stream=stream)
-        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n, stream=stream)
+    def fwd(b):
+        eg.engram_gate_fwd(b["x"], b["kv"], b["w"], b["m"], b["out"], b["saved"], n, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    def bwd(b):
+        eg.engram_gate_bwd(b["x"], b["kv"], b["w"], b["saved"], b["g"], b["gx"], b["gkv"], b["gw"], b["ws"], n,
+                           stream=stream)
+
+    for i in range(args.warmup):
+        fwd(sets[i % R])
+        bwd(sets[i % R])
     torch.cuda.synchronize()
 
     K = args.steps
@@ -160,10 +172,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        b = sets[i % R]
         ev[i][0].record(stream)
-        eg.engram_gate_fwd(x, kv, w, m, out, saved, n, stream=stream)
+        fwd(b)
         ev[i][1].record(stream)
-        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n, stream=stream)
+        bwd(b)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -201,7 +214,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "engram gate fwd+bwd, N=8192 tokens x 4 streams x 5120 (bf16 X/KV/grads, "
                                "fp32 weight/saved), mask Bernoulli(0.9), grad_out N(0,1), seed 0",
-                   "tokens": n, "streams": 4, "hidden": 5120, "mask_p": P_MASK},
+                   "tokens": n, "streams": 4, "hidden": 5120, "mask_p": P_MASK, "buffer_sets_rotated": R},
         "fwd": {"tokens_per_s": round(n / (fwd_ms * 1e-3), 1), "us": round(fwd_ms * 1e3, 2),
                 "tensor_gbps": round(fwd_gbps, 1), "frac_of_peak": round(fwd_gbps / PEAK_GBPS, 4)},
         "bwd": {"tokens_per_s": round(n / (bwd_ms * 1e-3), 1), "us": round(bwd_ms * 1e3, 2),
@@ -210,7 +223,8 @@ def main():
                     "tensor_gbps": round(both_gbps, 1), "frac_of_peak": round(both_gbps / PEAK_GBPS, 4)},
         "roofline": roof,
     }
-    del out, saved, gx, gkv, gw, ws, x, kv, g
+    sets.clear()
+    x = kv = w = m = g = b = None
     torch.cuda.empty_cache()
 
     if not args.no_large:
