@@ -80,7 +80,11 @@ typedef enum {
  *   weight [4][5120]    fp32, in       16-byte aligned
  *   mask   [N]          u8,   in       any alignment
  *   out    [N][4][5120] bf16, out      16-byte aligned
- *   saved  [N][4][4]    fp32, out      16-byte aligned
+ *   saved  [N][4][4]    fp32, out      16-byte aligned, or NULL for the
+ *                                      inference forward (nothing saved; out is
+ *                                      bit-identical to the saving call, as the
+ *                                      "tile-kernels 1.0.0" forward test requires
+ *                                      of save_for_backward=False)
  *   N      1 <= N <= 4194240
  * No workspace.  A false mask byte makes out[t] a bit copy of x[t] and saves
  * gate 0 for every stream of t; dot and both rstd are still saved.
@@ -107,6 +111,36 @@ engram_status engram_gate_fwd(const void *x, const void *kv, const float *weight
 engram_status engram_gate_bwd(const void *x, const void *kv, const float *weight, const float *saved,
                               const void *grad_out, void *grad_x, void *grad_kv, float *grad_weight,
                               void *workspace, int64_t N, void *stream);
+
+/*
+ * Backward plus the product rule of the fused weight.  Same arguments and
+ * contract as engram_gate_bwd, and in addition
+ *   wh, we   [4][5120] bf16, in   the source q/k normalisation weights with
+ *                                 weight == float(wh) * float(we)
+ *   grad_wh  [4][5120] fp32, out  grad_weight * float(we)  (one fp32 multiply)
+ *   grad_we  [4][5120] fp32, out  grad_weight * float(wh)
+ * grad_weight is still written.  The gate page leaves these gradients to the
+ * caller ("Engram saved-state gate", semantics paragraph); the
+ * "tile-kernels 1.0.0" backward test forms them this way.  They are produced
+ * by the grad_weight reduction kernel, so they cost no extra launch.
+ * All four extra pointers are required (ENGRAM_ERR_NULL otherwise), 16-byte
+ * aligned, and the outputs must not overlap anything.
+ */
+engram_status engram_gate_bwd_with_norm_weights(const void *x, const void *kv, const float *weight,
+                                                const float *saved, const void *grad_out, void *grad_x,
+                                                void *grad_kv, float *grad_weight, const void *wh,
+                                                const void *we, float *grad_wh, float *grad_we,
+                                                void *workspace, int64_t N, void *stream);
+
+/*
+ * Fused weight: weight = float(wh) * float(we), [4][5120] bf16 inputs, fp32
+ * output ("Engram saved-state gate", semantics paragraph: the weight argument
+ * is the FP32 product of the source q/k normalisation weights; the
+ * "tile-kernels 1.0.0" fused-weight test requires it bit-exact).  The product
+ * of two bf16 values is exact in fp32.  All pointers device, 16-byte aligned;
+ * weight must not overlap wh or we.
+ */
+engram_status engram_fused_weight(const void *wh, const void *we, float *weight, void *stream);
 
 /*
  * Workspace size of the backward in bytes ("Engram saved-state gate",

@@ -56,6 +56,10 @@ lib.engram_gate_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P]
 lib.engram_gate_fwd.restype = ctypes.c_int
 lib.engram_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
 lib.engram_gate_bwd.restype = ctypes.c_int
+lib.engram_gate_bwd_with_norm_weights.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
+lib.engram_gate_bwd_with_norm_weights.restype = ctypes.c_int
+lib.engram_fused_weight.argtypes = [_P, _P, _P, _P]
+lib.engram_fused_weight.restype = ctypes.c_int
 lib.engram_gate_bwd_workspace_bytes.argtypes = [_I64]
 lib.engram_gate_bwd_workspace_bytes.restype = ctypes.c_size_t
 lib.engram_status_string.argtypes = [ctypes.c_int]
@@ -108,7 +112,8 @@ def engram_gate_fwd(x, kv, weight, mask, out, saved, N=None, stream=None) -> Non
     """Enqueue the forward on `stream` (default: the current torch stream).
 
     x [N,4,5120] bf16, kv [N,25600] bf16, weight [4,5120] fp32, mask [N]
-    bool/uint8, out [N,4,5120] bf16 (written), saved [N,4,4] fp32 (written).
+    bool/uint8, out [N,4,5120] bf16 (written), saved [N,4,4] fp32 (written),
+    or saved=None for the inference forward.
     """
     if N is None:
         N = x.shape[0]
@@ -130,5 +135,22 @@ def engram_gate_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight
                                _ptr(grad_kv), _ptr(grad_weight), _ptr(workspace), N, _stream(stream, x)))
 
 
-__all__ = ["engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
+def engram_gate_bwd_with_norm_weights(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we,
+                                      grad_wh, grad_we, workspace, N=None, stream=None) -> None:
+    """engram_gate_bwd plus grad_wh = grad_weight * we and grad_we = grad_weight * wh
+    for weight = wh * we (wh, we [4,5120] bf16; grad_wh, grad_we [4,5120] fp32)."""
+    if N is None:
+        N = x.shape[0]
+    _check(lib.engram_gate_bwd_with_norm_weights(
+        _ptr(x), _ptr(kv), _ptr(weight), _ptr(saved), _ptr(grad_out), _ptr(grad_x), _ptr(grad_kv),
+        _ptr(grad_weight), _ptr(wh), _ptr(we), _ptr(grad_wh), _ptr(grad_we), _ptr(workspace), N,
+        _stream(stream, x)))
+
+
+def engram_fused_weight(wh, we, weight, stream=None) -> None:
+    """weight [4,5120] fp32 = float(wh) * float(we), wh and we [4,5120] bf16 (exact)."""
+    _check(lib.engram_fused_weight(_ptr(wh), _ptr(we), _ptr(weight), _stream(stream, wh)))
+
+
+__all__ = ["engram_gate_bwd_with_norm_weights", "engram_fused_weight", "engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
            "LIB_PATH"]

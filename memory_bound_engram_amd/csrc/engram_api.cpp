@@ -17,7 +17,7 @@ constexpr int64_t kXRowBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 2;  // 
 constexpr int64_t kKvRowBytes = (int64_t)ENGRAM_KV_COLS * 2;                 // 51200
 constexpr int64_t kWeightBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 4;  // 81920
 constexpr int64_t kSavedRowBytes = (int64_t)ENGRAM_STREAMS * 4 * 4;          // 64
-constexpr int kFwdWorkgroupsPerCu = 1;
+constexpr int kFwdWorkgroupsPerCu = 4;  // one resident per CU; the rest queue (measured ~2% faster at large N)
 constexpr int kMaxDevices = 64;
 
 thread_local int g_last_hip_error = 0;
@@ -32,7 +32,7 @@ Range range_of(const void* p, int64_t bytes) {
   return Range{a, a + (uintptr_t)bytes};
 }
 
-bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+bool overlaps(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -74,37 +74,72 @@ size_t engram_gate_bwd_workspace_bytes(int64_t N) {
 
 engram_status engram_gate_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
                               float* saved, int64_t N, void* stream) {
-  if (!x || !kv || !weight || !mask || !out || !saved) return ENGRAM_ERR_NULL;
+  // saved == NULL selects the inference forward (no saved state written)
+  if (!x || !kv || !weight || !mask || !out) return ENGRAM_ERR_NULL;
   if (N < 1 || N > ENGRAM_N_MAX) return ENGRAM_ERR_N_RANGE;
-  if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(out) || !aligned16(saved))
+  if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(out) || (saved && !aligned16(saved)))
     return ENGRAM_ERR_ALIGN;
   const Range in[] = {range_of(x, N * kXRowBytes), range_of(kv, N * kKvRowBytes), range_of(weight, kWeightBytes),
                       range_of(mask, N)};
-  const Range outs[] = {range_of(out, N * kXRowBytes), range_of(saved, N * kSavedRowBytes)};
+  const Range outs[] = {range_of(out, N * kXRowBytes), range_of(saved, saved ? N * kSavedRowBytes : 0)};
   if (any_overlap(in, 4, outs, 2)) return ENGRAM_ERR_OVERLAP;
   int64_t grid = (int64_t)kFwdWorkgroupsPerCu * cu_count();
   if (grid > N) grid = N;
   return launched(engram::launch_fwd(x, kv, weight, mask, out, saved, N, (int)grid, (hipStream_t)stream));
 }
 
-engram_status engram_gate_bwd(const void* x, const void* kv, const float* weight, const float* saved,
-                              const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight, void* workspace,
-                              int64_t N, void* stream) {
+static engram_status bwd_common(const void* x, const void* kv, const float* weight, const float* saved,
+                                const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight,
+                                const void* wh, const void* we, float* grad_wh, float* grad_we, void* workspace,
+                                int64_t N, void* stream) {
+  const bool rule = wh != nullptr;  // product-rule variant: all four extra pointers present
   if (!x || !kv || !weight || !saved || !grad_out || !grad_x || !grad_kv || !grad_weight || !workspace)
     return ENGRAM_ERR_NULL;
+  if (rule && (!we || !grad_wh || !grad_we)) return ENGRAM_ERR_NULL;
   if (N < 1 || N > ENGRAM_BWD_N_MAX) return ENGRAM_ERR_N_RANGE;
   if (N % ENGRAM_BWD_N_MULTIPLE != 0) return ENGRAM_ERR_N_MULT64;
   if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(saved) || !aligned16(grad_out) ||
       !aligned16(grad_x) || !aligned16(grad_kv) || !aligned16(grad_weight) || !aligned16(workspace))
     return ENGRAM_ERR_ALIGN;
-  const Range in[] = {range_of(x, N * kXRowBytes), range_of(kv, N * kKvRowBytes), range_of(weight, kWeightBytes),
-                      range_of(saved, N * kSavedRowBytes), range_of(grad_out, N * kXRowBytes)};
+  if (rule && (!aligned16(wh) || !aligned16(we) || !aligned16(grad_wh) || !aligned16(grad_we)))
+    return ENGRAM_ERR_ALIGN;
+  const int64_t nw = rule ? kWeightBytes / 2 : 0;  // bf16 norm weights
+  const int64_t gw = rule ? kWeightBytes : 0;
+  const Range in[] = {range_of(x, N * kXRowBytes),      range_of(kv, N * kKvRowBytes),
+                      range_of(weight, kWeightBytes),   range_of(saved, N * kSavedRowBytes),
+                      range_of(grad_out, N * kXRowBytes), range_of(wh, nw), range_of(we, nw)};
   const Range outs[] = {range_of(grad_x, N * kXRowBytes), range_of(grad_kv, N * kKvRowBytes),
                         range_of(grad_weight, kWeightBytes),
-                        range_of(workspace, (int64_t)engram_gate_bwd_workspace_bytes(N))};
-  if (any_overlap(in, 5, outs, 4)) return ENGRAM_ERR_OVERLAP;
-  return launched(engram::launch_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace, N,
-                                     (hipStream_t)stream));
+                        range_of(workspace, (int64_t)engram_gate_bwd_workspace_bytes(N)),
+                        range_of(grad_wh, gw), range_of(grad_we, gw)};
+  if (any_overlap(in, 7, outs, 6)) return ENGRAM_ERR_OVERLAP;
+  return launched(engram::launch_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we, grad_wh,
+                                     grad_we, workspace, N, (hipStream_t)stream));
+}
+
+engram_status engram_gate_bwd(const void* x, const void* kv, const float* weight, const float* saved,
+                              const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight, void* workspace,
+                              int64_t N, void* stream) {
+  return bwd_common(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, nullptr, nullptr, nullptr, nullptr,
+                    workspace, N, stream);
+}
+
+engram_status engram_gate_bwd_with_norm_weights(const void* x, const void* kv, const float* weight, const float* saved,
+                                                const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight,
+                                                const void* wh, const void* we, float* grad_wh, float* grad_we,
+                                                void* workspace, int64_t N, void* stream) {
+  if (!wh) return ENGRAM_ERR_NULL;
+  return bwd_common(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we, grad_wh, grad_we, workspace,
+                    N, stream);
+}
+
+engram_status engram_fused_weight(const void* wh, const void* we, float* weight, void* stream) {
+  if (!wh || !we || !weight) return ENGRAM_ERR_NULL;
+  if (!aligned16(wh) || !aligned16(we) || !aligned16(weight)) return ENGRAM_ERR_ALIGN;
+  const Range in[] = {range_of(wh, kWeightBytes / 2), range_of(we, kWeightBytes / 2)};
+  const Range outs[] = {range_of(weight, kWeightBytes)};
+  if (any_overlap(in, 2, outs, 1)) return ENGRAM_ERR_OVERLAP;
+  return launched(engram::launch_fused_weight(wh, we, weight, (hipStream_t)stream));
 }
 
 const char* engram_status_string(int status) {

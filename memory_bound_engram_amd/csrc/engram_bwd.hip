@@ -34,7 +34,11 @@
 // order at the end.
 // Kernel 2 (reduce): grad_weight[s][j] = sum over rows of the partials, in a
 // fixed order (8 contiguous row chunks summed sequentially, then the chunk
-// sums added in chunk order), so the result is bitwise reproducible.
+// sums added in chunk order), so the result is bitwise reproducible.  When
+// the source norm weights wh, we (weight = wh * we) are given, the same
+// kernel also writes their product-rule gradients grad_wh = grad_weight * we
+// and grad_we = grad_weight * wh ("tile-kernels 1.0.0" listing,
+// test_engram_gate_bwd.py; the gate page leaves this step to the caller).
 //
 // Workspace layout (size fixed by the workspace paragraph): the first 16*N
 // floats are reserved for per-(token, stream) scalars and are unused by this
@@ -216,7 +220,9 @@ constexpr int kReduceThreads = kReduceChunks * kReduceGroups;  // 256
 constexpr int kReduceCols4 = kStreams * kHidden / 4;     // 5120 float4 columns
 
 __global__ void __launch_bounds__(kReduceThreads)
-engram_bwd_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dw, int nb) {
+engram_bwd_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dw, int nb,
+                         const uint16_t* __restrict__ wh, const uint16_t* __restrict__ we,
+                         float* __restrict__ gwh, float* __restrict__ gwe) {
   __shared__ f32x4 part[kReduceChunks][kReduceGroups];
   const int g = threadIdx.x % kReduceGroups;
   const int q = threadIdx.x / kReduceGroups;
@@ -233,11 +239,49 @@ engram_bwd_reduce_kernel(const float* __restrict__ partial, float* __restrict__ 
 #pragma unroll
     for (int k = 1; k < kReduceChunks; ++k) r += part[k][g];
     reinterpret_cast<f32x4*>(dw)[col4] = r;
+    if (gwh) {
+      // product rule for weight = wh * we (both bf16): one fp32 multiply each
+      const uint2 h = reinterpret_cast<const uint2*>(wh)[col4];
+      const uint2 e = reinterpret_cast<const uint2*>(we)[col4];
+      const f32x4 hf = {bf_lo(h.x), bf_hi(h.x), bf_lo(h.y), bf_hi(h.y)};
+      const f32x4 ef = {bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
+      reinterpret_cast<f32x4*>(gwh)[col4] = r * ef;
+      reinterpret_cast<f32x4*>(gwe)[col4] = r * hf;
+    }
   }
 }
 
+// weight = float(wh) * float(we): the product of two bf16 values (8-bit
+// significands) is exact in fp32, so this is bit-exact by construction.
+__global__ void __launch_bounds__(256)
+engram_fused_weight_kernel(const uint16_t* __restrict__ wh, const uint16_t* __restrict__ we,
+                           float* __restrict__ weight) {
+  const int v = blockIdx.x * 256 + threadIdx.x;  // one 8-element vector; grid covers 2560 exactly
+  const u32x4 h = load16(wh + v * kVec);
+  const u32x4 e = load16(we + v * kVec);
+  f32x4 lo, hi;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    lo[2 * q] = bf_lo(h[q]) * bf_lo(e[q]);
+    lo[2 * q + 1] = bf_hi(h[q]) * bf_hi(e[q]);
+    hi[2 * q] = bf_lo(h[q + 2]) * bf_lo(e[q + 2]);
+    hi[2 * q + 1] = bf_hi(h[q + 2]) * bf_hi(e[q + 2]);
+  }
+  reinterpret_cast<f32x4*>(weight)[2 * v] = lo;
+  reinterpret_cast<f32x4*>(weight)[2 * v + 1] = hi;
+}
+
+hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hipStream_t stream) {
+  const uint16_t* hp = static_cast<const uint16_t*>(wh);
+  const uint16_t* ep = static_cast<const uint16_t*>(we);
+  void* args[] = {&hp, &ep, &weight};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&engram_fused_weight_kernel),
+                         dim3(kStreams * kRowVecs / 256), dim3(256), args, 0, stream);
+}
+
 hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const float* saved, const void* gout,
-                      void* dx, void* dkv, float* dw, void* workspace, int64_t n, hipStream_t stream) {
+                      void* dx, void* dkv, float* dw, const void* wh, const void* we, float* gwh, float* gwe,
+                      void* workspace, int64_t n, hipStream_t stream) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* kvp = static_cast<const uint16_t*>(kv);
   const uint16_t* gp = static_cast<const uint16_t*>(gout);
@@ -252,7 +296,9 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
                                  dim3(kBwdThreads), args1, 0, stream);
   if (e != hipSuccess) return e;
   const float* cpartial = partial;
-  void* args2[] = {&cpartial, &dw, &nbv};
+  const uint16_t* whp = static_cast<const uint16_t*>(wh);
+  const uint16_t* wep = static_cast<const uint16_t*>(we);
+  void* args2[] = {&cpartial, &dw, &nbv, &whp, &wep, &gwh, &gwe};
   return hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_reduce_kernel),
                          dim3(kReduceCols4 / kReduceGroups), dim3(kReduceThreads), args2, 0, stream);
 }

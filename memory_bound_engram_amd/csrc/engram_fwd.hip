@@ -29,6 +29,9 @@ namespace engram {
 constexpr int kFwdThreads = 64 * kStreams;   // one wave per stream
 constexpr int kFwdVecs = kRowVecs / 64;      // 10 vectors per lane per row
 
+// kSave = false is the inference forward: saved is not written; out is
+// bit-identical to the saving path (same arithmetic).
+template <bool kSave>
 __global__ void __launch_bounds__(kFwdThreads)
 engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
                   const float* __restrict__ weight, const uint8_t* __restrict__ mask,
@@ -107,7 +110,7 @@ engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ k
       }
       store16_stream(os + (lane + 64 * i) * kVec, o);
     }
-    if (lane == 0) {
+    if (kSave && lane == 0) {
       const f32x4 sv = {m ? gate : 0.f, dot, rx, rk};
       *reinterpret_cast<f32x4*>(saved + t * (kStreams * 4) + 4 * s) = sv;
     }
@@ -120,8 +123,9 @@ hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const 
   const uint16_t* kvp = static_cast<const uint16_t*>(kv);
   uint16_t* op = static_cast<uint16_t*>(out);
   void* args[] = {&xp, &kvp, &weight, &mask, &op, &saved, &n};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&engram_fwd_kernel), dim3(grid), dim3(kFwdThreads), args,
-                         0, stream);
+  const void* fn = saved ? reinterpret_cast<const void*>(&engram_fwd_kernel<true>)
+                         : reinterpret_cast<const void*>(&engram_fwd_kernel<false>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kFwdThreads), args, 0, stream);
 }
 
 }  // namespace engram

@@ -63,6 +63,10 @@ def _load():
         for f in (lib.engram_oracle_fwd_f64, lib.engram_oracle_bwd_f64,
                   lib.engram_oracle_fwd_bf16, lib.engram_oracle_bwd_bf16):
             f.restype = ctypes.c_int
+        lib.engram_oracle_fused_weight.argtypes = [I64, P, P, P]
+        lib.engram_oracle_fused_weight.restype = ctypes.c_int
+        lib.engram_oracle_weight_grads.argtypes = [I64, P, P, P, P, P]
+        lib.engram_oracle_weight_grads.restype = ctypes.c_int
         lib.engram_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.engram_oracle_f32_to_bf16.restype = ctypes.c_uint16
         _lib = lib
@@ -189,3 +193,28 @@ def bwd_bf16(x16, kv16, w32, saved32, g16, threads: int = 1, extras: bool = Fals
 
 def f32_to_bf16(f: float) -> int:
     return int(_load().engram_oracle_f32_to_bf16(ctypes.c_float(f)))
+
+
+def fused_weight(wh16, we16):
+    """weight fp32 = fp32(wh) * fp32(we) for bf16-bit arrays of equal shape."""
+    wh16 = _arr(wh16, np.uint16)
+    we16 = _arr(we16, np.uint16)
+    assert wh16.shape == we16.shape
+    out = np.empty(wh16.shape, np.float32)
+    rc = _load().engram_oracle_fused_weight(wh16.size, _ptr(wh16), _ptr(we16), _ptr(out))
+    if rc != 0:
+        raise RuntimeError(f"oracle fused_weight failed: {rc}")
+    return out
+
+
+def weight_grads(dw64, wh16, we16):
+    """Product rule of weight = wh * we: returns (grad_wh, grad_we) in fp64."""
+    dw64 = _arr(dw64, np.float64)
+    wh16 = _arr(wh16, np.uint16)
+    we16 = _arr(we16, np.uint16)
+    gwh = np.empty(dw64.shape, np.float64)
+    gwe = np.empty(dw64.shape, np.float64)
+    rc = _load().engram_oracle_weight_grads(dw64.size, _ptr(dw64), _ptr(wh16), _ptr(we16), _ptr(gwh), _ptr(gwe))
+    if rc != 0:
+        raise RuntimeError(f"oracle weight_grads failed: {rc}")
+    return gwh, gwe

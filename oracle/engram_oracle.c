@@ -568,3 +568,34 @@ int engram_oracle_bwd_bf16(int64_t d, int64_t n, const uint16_t *x, const uint16
 
 /* Exposed so the tests can pin the conversion itself against its definition. */
 uint16_t engram_oracle_f32_to_bf16(float f) { return float_to_bf16_rne(f); }
+
+/* ---- fused weight and its product rule ---- */
+
+/*
+ * weight = fp32(wh) * fp32(we) for bf16 inputs ("Engram saved-state gate",
+ * semantics paragraph: the weight argument is the FP32 product of the source
+ * q/k normalisation weights).  Formed in fp64 and rounded to fp32; for
+ * normal-range inputs the product has at most 16 significant bits, so both
+ * steps are exact.
+ */
+int engram_oracle_fused_weight(int64_t count, const uint16_t *wh, const uint16_t *we, float *weight) {
+  if (count < 0 || (count > 0 && (!wh || !we || !weight))) return -1;
+  for (int64_t q = 0; q < count; ++q) weight[q] = (float)(bf16_bits_to_double(wh[q]) * bf16_bits_to_double(we[q]));
+  return 0;
+}
+
+/*
+ * Product rule of weight = wh * we: with G_w = dL/dweight,
+ *   dL/dwh = G_w * we,  dL/dwe = G_w * wh      (fp64, no rounding)
+ * The gate page leaves this to the caller; the "tile-kernels 1.0.0" backward
+ * test forms it this way from the summed grad_weight.
+ */
+int engram_oracle_weight_grads(int64_t count, const double *dw, const uint16_t *wh, const uint16_t *we,
+                               double *grad_wh, double *grad_we) {
+  if (count < 0 || (count > 0 && (!dw || !wh || !we || !grad_wh || !grad_we))) return -1;
+  for (int64_t q = 0; q < count; ++q) {
+    grad_wh[q] = dw[q] * bf16_bits_to_double(we[q]);
+    grad_we[q] = dw[q] * bf16_bits_to_double(wh[q]);
+  }
+  return 0;
+}

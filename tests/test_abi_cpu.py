@@ -84,11 +84,24 @@ def call_fwd(a, n):
     return eg.lib.engram_gate_fwd(a["x"], a["kv"], a["w"], a["m"], a["out"], a["sv"], n, None)
 
 
-@pytest.mark.parametrize("field", ["x", "kv", "w", "m", "out", "sv"])
+@pytest.mark.parametrize("field", ["x", "kv", "w", "m", "out"])
 def test_fwd_rejects_null(field):
     a = fwd_layout(8)
     a[field] = None
     assert call_fwd(a, 8) == eg.ERR_NULL
+
+
+def test_fwd_without_saved_is_still_validated():
+    # saved == NULL selects the inference forward; everything else is checked
+    a = fwd_layout(8)
+    a["sv"] = None
+    a["x"] += 4
+    assert call_fwd(a, 8) == eg.ERR_ALIGN
+    a = fwd_layout(8)
+    a["sv"] = None
+    a["out"] = a["kv"]
+    assert call_fwd(a, 8) == eg.ERR_OVERLAP
+    assert call_fwd(dict(fwd_layout(8), sv=None), 0) == eg.ERR_N_RANGE
 
 
 @pytest.mark.parametrize("n", [0, -1, 4194241, 1 << 40])
@@ -176,3 +189,59 @@ def test_bwd_inputs_may_alias_each_other():
 def test_status_strings():
     for s in range(7):
         assert eg.lib.engram_status_string(s)
+
+
+# ---------------- backward with the product rule; fused weight ----------------
+
+def nw_layout(n):
+    a = bwd_layout(n)
+    p = max(a.values()) + (1 << 30)
+    for name, size in (("wh", WB // 2), ("we", WB // 2), ("gwh", WB), ("gwe", WB)):
+        a[name] = p
+        p += size + 4096
+    return a
+
+
+def call_nw(a, n):
+    return eg.lib.engram_gate_bwd_with_norm_weights(a["x"], a["kv"], a["w"], a["sv"], a["g"], a["dx"], a["dkv"],
+                                                    a["dw"], a["wh"], a["we"], a["gwh"], a["gwe"], a["ws"], n,
+                                                    None)
+
+
+@pytest.mark.parametrize("field", ["wh", "we", "gwh", "gwe", "x", "ws"])
+def test_bwd_norm_weights_rejects_null(field):
+    a = nw_layout(64)
+    a[field] = None
+    assert call_nw(a, 64) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("field", ["wh", "we", "gwh", "gwe"])
+def test_bwd_norm_weights_rejects_misaligned(field):
+    a = nw_layout(64)
+    a[field] += 2
+    assert call_nw(a, 64) == eg.ERR_ALIGN
+
+
+@pytest.mark.parametrize("out,other", [("gwh", "wh"), ("gwe", "we"), ("gwh", "gwe"), ("gwh", "dw"),
+                                       ("gwe", "x"), ("dx", "wh")])
+def test_bwd_norm_weights_rejects_overlap(out, other):
+    a = nw_layout(64)
+    a[out] = a[other]
+    assert call_nw(a, 64) == eg.ERR_OVERLAP
+
+
+def test_bwd_norm_weights_checks_n():
+    assert call_nw(nw_layout(64), 100) == eg.ERR_N_MULT64
+    assert call_nw(nw_layout(64), 8256) == eg.ERR_N_RANGE
+
+
+def test_fused_weight_validation():
+    f = eg.lib.engram_fused_weight
+    wh, we, w = BASE, BASE + (1 << 20), BASE + (2 << 20)
+    assert f(None, we, w, None) == eg.ERR_NULL
+    assert f(wh, None, w, None) == eg.ERR_NULL
+    assert f(wh, we, None, None) == eg.ERR_NULL
+    assert f(wh + 2, we, w, None) == eg.ERR_ALIGN
+    assert f(wh, we, w + 8, None) == eg.ERR_ALIGN
+    assert f(wh, we, wh, None) == eg.ERR_OVERLAP
+    assert f(wh, we, we + 1024, None) == eg.ERR_OVERLAP

@@ -38,6 +38,10 @@ MUTANTS = [
      "fwd_token(d, x, kv, kv + 3 * d, w, m, out, sv, aux);"),
     ("bf16 rounding half-up instead of ties-to-even", "u += 0x7fffu + ((u >> 16) & 1u);", "u += 0x8000u;"),
     ("dot over raw (unnormalised) key", "(xs[j] * rx) * ws[j] * (ks[j] * rk)", "(xs[j] * rx) * ws[j] * ks[j]"),
+    ("product rule uses the wrong factor", "grad_wh[q] = dw[q] * bf16_bits_to_double(we[q]);",
+     "grad_wh[q] = dw[q] * bf16_bits_to_double(wh[q]);"),
+    ("fused weight drops a factor", "weight[q] = (float)(bf16_bits_to_double(wh[q]) * bf16_bits_to_double(we[q]));",
+     "weight[q] = (float)(bf16_bits_to_double(wh[q]));"),
 ]
 
 

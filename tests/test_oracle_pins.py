@@ -404,3 +404,48 @@ def test_backward_matches_central_differences_d5120():
             flat[i] = base[i]
             fd = (lp - lm) / (2 * h)
             assert abs(fd - gflat[i]) <= 1e-5 * max(abs(gflat[i]), 1e-2), (name, int(i), fd, gflat[i])
+
+
+# --------------------------------------------------------------------------
+# fused weight = wh * we and its product rule
+# --------------------------------------------------------------------------
+
+def test_fused_weight_is_the_exact_product():
+    """bf16 x bf16 has at most 16 significant bits: exact in fp32."""
+    from fractions import Fraction
+    wh = synth.normal_bf16(4 * 64, 3, 21).reshape(4, 64)
+    we = synth.normal_bf16(4 * 64, 3, 22).reshape(4, 64)
+    got = oracle.fused_weight(wh, we)
+    a, b = bf16_to_f64(wh).ravel(), bf16_to_f64(we).ravel()
+    for i in range(a.size):
+        assert Fraction(float(got.ravel()[i])) == Fraction(a[i]) * Fraction(b[i])
+
+
+def test_product_rule_matches_central_differences():
+    """dL/dwh and dL/dwe through weight = wh * we, against fp64 differences of
+    the forward evaluated with the composed weight."""
+    n, d, h = 2, 8, 1e-6
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((n, 4, d))
+    kv = rng.standard_normal((n, 5 * d))
+    G = rng.standard_normal((n, 4, d))
+    mask = np.ones(n, np.uint8)
+    wh16 = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal((4, d))).astype(np.float32))
+    we16 = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal((4, d))).astype(np.float32))
+    wh, we = bf16_to_f64(wh16), bf16_to_f64(we16)
+    w = wh * we
+    _, sv = oracle.fwd_f64(x, kv, w, mask)
+    assert np.all(np.abs(sv[:, :, 1]) > 1e-2)
+    _, _, dw = oracle.bwd_f64(x, kv, w, sv, G)
+    gwh, gwe = oracle.weight_grads(dw, wh16, we16)
+
+    def loss(a, b):
+        out, _ = oracle.fwd_f64(x, kv, a * b, mask)
+        return float(np.sum(G * out))
+
+    for (s_, j) in [(0, 0), (1, 3), (3, 7), (2, 5)]:
+        e = np.zeros((4, d)); e[s_, j] = h
+        fd_h = (loss(wh + e, we) - loss(wh - e, we)) / (2 * h)
+        fd_e = (loss(wh, we + e) - loss(wh, we - e)) / (2 * h)
+        assert abs(fd_h - gwh[s_, j]) <= 1e-5 * max(abs(gwh[s_, j]), 1e-2)
+        assert abs(fd_e - gwe[s_, j]) <= 1e-5 * max(abs(gwe[s_, j]), 1e-2)
