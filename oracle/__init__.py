@@ -67,6 +67,12 @@ def _load():
         lib.engram_oracle_fused_weight.restype = ctypes.c_int
         lib.engram_oracle_weight_grads.argtypes = [I64, P, P, P, P, P]
         lib.engram_oracle_weight_grads.restype = ctypes.c_int
+        lib.engram_oracle_gateconv_fwd_f64.argtypes = [I64, I64, I64, ctypes.c_double] + [P] * 13
+        lib.engram_oracle_gateconv_fwd_f64.restype = ctypes.c_int
+        lib.engram_oracle_gateconv_bwd_f64.argtypes = [I64, I64, I64] + [P] * 24
+        lib.engram_oracle_gateconv_bwd_f64.restype = ctypes.c_int
+        lib.engram_oracle_round_bf16.argtypes = [I64, P, P]
+        lib.engram_oracle_round_bf16.restype = ctypes.c_int
         lib.engram_oracle_f32_to_bf16.argtypes = [ctypes.c_float]
         lib.engram_oracle_f32_to_bf16.restype = ctypes.c_uint16
         _lib = lib
@@ -218,3 +224,60 @@ def weight_grads(dw64, wh16, we16):
     if rc != 0:
         raise RuntimeError(f"oracle weight_grads failed: {rc}")
     return gwh, gwe
+
+
+# ---------------- Engram GateConv (TileOPs "Engram Operators" page) ----------------
+
+GATECONV_TAPS = 4
+
+
+def round_bf16(x64):
+    """fp64 -> fp32 (RNE) -> bf16 (RNE) bits."""
+    x64 = _arr(x64, np.float64)
+    out = np.empty(x64.shape, np.uint16)
+    rc = _load().engram_oracle_round_bf16(x64.size, _ptr(x64), _ptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle round_bf16 failed")
+    return out
+
+
+def gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=1e-6, mags=False):
+    """GateConv forward in fp64.  H, k, v [M,T,d]; wh, wv [d]; cw [4,d].
+
+    Returns (Y, vhat, alpha, rrms_h, rrms_k, rrms_v) [+ magY].
+    """
+    H, k, v = (_arr(a, np.float64) for a in (H, k, v))
+    wh, wv, cw = (_arr(a, np.float64) for a in (wh, wv, cw))
+    M, T, d = H.shape
+    assert k.shape == v.shape == H.shape and wh.shape == wv.shape == (d,) and cw.shape == (GATECONV_TAPS, d)
+    Y, vhat = np.empty_like(H), np.empty_like(H)
+    al, rh, rk, rv = (np.empty((M, T), np.float64) for _ in range(4))
+    mY = np.empty_like(H) if mags else None
+    rc = _load().engram_oracle_gateconv_fwd_f64(M, T, d, eps, _ptr(H), _ptr(k), _ptr(v), _ptr(wh), _ptr(wv),
+                                                _ptr(cw), _ptr(Y), _ptr(vhat), _ptr(al), _ptr(rh), _ptr(rk),
+                                                _ptr(rv), _ptr(mY))
+    if rc != 0:
+        raise RuntimeError(f"oracle gateconv_fwd_f64 failed: {rc}")
+    return (Y, vhat, al, rh, rk, rv) + ((mY,) if mags else ())
+
+
+def gateconv_bwd_f64(dY, H, k, v, wh, wv, cw, vhat, alpha, rrh, rrk, rrv, mags=False):
+    """GateConv backward in fp64 from the saved tensors.
+
+    Returns (dH, dk, dv, dwh, dwv, dcw) [+ (magH, magk, magv, mdwh, mdwv, mdcw)].
+    """
+    dY, H, k, v, vhat = (_arr(a, np.float64) for a in (dY, H, k, v, vhat))
+    wh, wv, cw = (_arr(a, np.float64) for a in (wh, wv, cw))
+    alpha, rrh, rrk, rrv = (_arr(a, np.float64) for a in (alpha, rrh, rrk, rrv))
+    M, T, d = H.shape
+    dH, dk, dv = np.empty_like(H), np.empty_like(H), np.empty_like(H)
+    dwh, dwv, dcw = np.empty(d), np.empty(d), np.empty((GATECONV_TAPS, d))
+    m = ((np.empty_like(H), np.empty_like(H), np.empty_like(H), np.empty(d), np.empty(d),
+          np.empty((GATECONV_TAPS, d))) if mags else (None,) * 6)
+    rc = _load().engram_oracle_gateconv_bwd_f64(M, T, d, _ptr(dY), _ptr(H), _ptr(k), _ptr(v), _ptr(wh), _ptr(wv),
+                                                _ptr(cw), _ptr(vhat), _ptr(alpha), _ptr(rrh), _ptr(rrk), _ptr(rrv),
+                                                _ptr(dH), _ptr(dk), _ptr(dv), _ptr(dwh), _ptr(dwv), _ptr(dcw),
+                                                *[_ptr(x) for x in m])
+    if rc != 0:
+        raise RuntimeError(f"oracle gateconv_bwd_f64 failed: {rc}")
+    return (dH, dk, dv, dwh, dwv, dcw) + (m if mags else ())

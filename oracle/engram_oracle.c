@@ -599,3 +599,261 @@ int engram_oracle_weight_grads(int64_t count, const double *dw, const uint16_t *
   }
   return 0;
 }
+
+/* ======================================================================
+ * Engram GateConv ("Engram Operators", TileOPs; GateConv section).
+ *
+ * The page gives the stages (RMSNorm gating -> causal depthwise conv1d ->
+ * SiLU + residual), the shapes and the saved tensors, but no formulas.
+ * Readings (the plainest the page supports):
+ *   G1  h^ = H rrms_h w_h, k^ = k rrms_k w_h: one RMSNorm weight for H and k,
+ *       rrms = (mean of squares + eps)^(-1/2), eps default 1e-6.
+ *   G2  alpha = sigmoid(<h^, k^> / sqrt(d)), one scalar per (m, t).
+ *   G3  vhat = alpha v (the gated value; saved).
+ *   G4  u = vhat rrms_v w_v, rrms_v the reciprocal RMS of vhat (saved).
+ *   G5  c[t] = sum_{i<4} conv_w[i] u[t-3+i], causal within each sequence m,
+ *       zero history before t = 0, dilation 1 (the op has no dilation).
+ *   G6  Y = SiLU(c) + vhat, SiLU(c) = c sigmoid(c).
+ * Layout: H, k, v, Y, vhat, dY, dH, dk, dv [M][T][d]; alpha, rrms_* [M][T];
+ * w_h, w_v [d]; conv_w [4][d].
+ *
+ * Magnitude outputs (for tolerances only): a first-order bound m(q) of the
+ * terms that build each output, so that an fp32 evaluation errs by a modest
+ * multiple of 2^-24 m(q): m(a+b) = m(a)+m(b), m(ab) = m(a)m(b), and a scalar
+ * map f adds |f'(x)| m(x) to |f(x)|.
+ * ====================================================================== */
+
+#define GC_TAPS 4
+
+static double silu(double c) { return c * sigmoid(c); }
+static double silu_grad(double c) {
+  const double s = sigmoid(c);
+  return s * (1.0 + c * (1.0 - s));
+}
+
+/*
+ * Forward for one sequence of T tokens (fp64).  u_scr and um_scr are
+ * scratch of T*d doubles, da_scr of T doubles.  magY may be NULL.
+ */
+static void gateconv_fwd_seq(int64_t T, int64_t d, double eps, const double *H, const double *k, const double *v,
+                             const double *wh, const double *wv, const double *cw, double *Y, double *vhat,
+                             double *alpha, double *rrh, double *rrk, double *rrv, double *magY, double *u_scr,
+                             double *um_scr, double *da_scr) {
+  const double sd = sqrt((double)d);
+  for (int64_t t = 0; t < T; ++t) {
+    const double *Ht = H + t * d, *kt = k + t * d, *vt = v + t * d;
+    double shh = 0.0, skk = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      shh += Ht[j] * Ht[j];
+      skk += kt[j] * kt[j];
+    }
+    const double rh = 1.0 / sqrt(shh / (double)d + eps), rk = 1.0 / sqrt(skk / (double)d + eps); /* G1 */
+    double s = 0.0, smag = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      const double term = (Ht[j] * rh * wh[j]) * (kt[j] * rk * wh[j]);
+      s += term;
+      smag += fabs(term);
+    }
+    s /= sd; /* G2 */
+    smag /= sd;
+    const double a = sigmoid(s);
+    da_scr[t] = a * (1.0 - a) * smag; /* magnitude of alpha's error term */
+    double svv = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      vhat[t * d + j] = a * vt[j]; /* G3 */
+      svv += vhat[t * d + j] * vhat[t * d + j];
+    }
+    const double rv = 1.0 / sqrt(svv / (double)d + eps); /* G4 */
+    for (int64_t j = 0; j < d; ++j) {
+      u_scr[t * d + j] = vhat[t * d + j] * rv * wv[j];
+      /* alpha enters u directly and through rrms_v (at most as strongly again) */
+      um_scr[t * d + j] = fabs(u_scr[t * d + j]) * (1.0 + (a > 0.0 ? 2.0 * da_scr[t] / a : 0.0));
+    }
+    alpha[t] = a;
+    rrh[t] = rh;
+    rrk[t] = rk;
+    rrv[t] = rv;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t j = 0; j < d; ++j) {
+      double c = 0.0, cm = 0.0;
+      for (int i = 0; i < GC_TAPS; ++i) { /* G5 */
+        const int64_t tau = t - (GC_TAPS - 1) + i;
+        if (tau < 0) continue;
+        c += cw[(int64_t)i * d + j] * u_scr[tau * d + j];
+        cm += fabs(cw[(int64_t)i * d + j]) * um_scr[tau * d + j];
+      }
+      Y[t * d + j] = silu(c) + vhat[t * d + j]; /* G6 */
+      if (magY)
+        magY[t * d + j] = fabs(silu(c)) + fabs(silu_grad(c)) * cm + fabs(vhat[t * d + j]) +
+                          fabs(v[t * d + j]) * da_scr[t];
+    }
+  }
+}
+
+/*
+ * Forward, fp64 in and out.  Returns 0, or -1 for bad arguments, -2 when out
+ * of memory.  magY may be NULL.
+ */
+int engram_oracle_gateconv_fwd_f64(int64_t M, int64_t T, int64_t d, double eps, const double *H, const double *k,
+                                   const double *v, const double *wh, const double *wv, const double *cw, double *Y,
+                                   double *vhat, double *alpha, double *rrh, double *rrk, double *rrv,
+                                   double *magY) {
+  if (M < 0 || T < 0 || d < 1) return -1;
+  if (M * T > 0 && (!H || !k || !v || !wh || !wv || !cw || !Y || !vhat || !alpha || !rrh || !rrk || !rrv))
+    return -1;
+  double *scr = (double *)malloc(((size_t)2 * T * d + (size_t)T + 1) * sizeof(double));
+  if (!scr) return -2;
+  for (int64_t m = 0; m < M; ++m) {
+    const int64_t o = m * T * d, os = m * T;
+    gateconv_fwd_seq(T, d, eps, H + o, k + o, v + o, wh, wv, cw, Y + o, vhat + o, alpha + os, rrh + os, rrk + os,
+                     rrv + os, magY ? magY + o : NULL, scr, scr + T * d, scr + 2 * T * d);
+  }
+  free(scr);
+  return 0;
+}
+
+/*
+ * Backward for one sequence, from the saved tensors (vhat, alpha, rrms_h,
+ * rrms_k, rrms_v), as the page's backward op takes them.  Gradient of
+ * L = sum dY * Y through G1..G6:
+ *   u_t   = vhat_t rrms_v w_v;  c_t = sum_i cw_i u_{t-3+i}
+ *   dc_t  = dY_t SiLU'(c_t);    dcw_i += dc_t u_{t-3+i}
+ *   du_t  = sum_i cw_i dc_{t+3-i}
+ *   dwv  += du_t vhat_t rrms_v
+ *   dvhat = dY_t + rrms_v (w_v du_t - vhat_t rrms_v^2 <du_t w_v, vhat_t> / d)
+ *   dalpha = <dvhat, v_t>;  dv = alpha dvhat;  ds = dalpha alpha (1 - alpha)
+ *   dh^ = ds k^ / sqrt(d);  dk^ = ds h^ / sqrt(d)
+ *   dH  = rrms_h (w_h dh^ - H rrms_h^2 <dh^ w_h, H> / d)     (likewise dk)
+ *   dwh += dh^ H rrms_h + dk^ k rrms_k
+ * Scratch: 3*T*d + 2*T doubles.  Accumulates dwh, dwv, dcw (and their
+ * magnitudes when mag* are given).
+ */
+static void gateconv_bwd_seq(int64_t T, int64_t d, const double *dY, const double *H, const double *k,
+                             const double *v, const double *wh, const double *wv, const double *cw,
+                             const double *vhat, const double *alpha, const double *rrh, const double *rrk,
+                             const double *rrv, double *dH, double *dk, double *dv, double *dwh, double *dwv,
+                             double *dcw, double *magH, double *magk, double *magv, double *mdwh, double *mdwv,
+                             double *mdcw, double *scr) {
+  const double sd = sqrt((double)d);
+  double *u = scr, *dc = scr + T * d, *dcm = scr + 2 * T * d;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < d; ++j) u[t * d + j] = vhat[t * d + j] * rrv[t] * wv[j];
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < d; ++j) {
+      double c = 0.0, cm = 0.0;
+      for (int i = 0; i < GC_TAPS; ++i) {
+        const int64_t tau = t - (GC_TAPS - 1) + i;
+        if (tau < 0) continue;
+        c += cw[(int64_t)i * d + j] * u[tau * d + j];
+        cm += fabs(cw[(int64_t)i * d + j] * u[tau * d + j]);
+      }
+      const double g = silu_grad(c);
+      /* SiLU'' is bounded by 0.5: error of c moves dc by at most |dY| 0.5 m(c) */
+      dc[t * d + j] = dY[t * d + j] * g;
+      dcm[t * d + j] = fabs(dY[t * d + j]) * (fabs(g) + 0.5 * cm);
+      for (int i = 0; i < GC_TAPS; ++i) {
+        const int64_t tau = t - (GC_TAPS - 1) + i;
+        if (tau < 0) continue;
+        dcw[(int64_t)i * d + j] += dc[t * d + j] * u[tau * d + j];
+        if (mdcw) mdcw[(int64_t)i * d + j] += dcm[t * d + j] * fabs(u[tau * d + j]);
+      }
+    }
+  for (int64_t t = 0; t < T; ++t) {
+    const double *Ht = H + t * d, *kt = k + t * d, *vt = v + t * d, *vh = vhat + t * d;
+    const double a = alpha[t], rh = rrh[t], rk = rrk[t], rv = rrv[t];
+    /* du_t and the first row sum */
+    double s1 = 0.0, s1m = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      double du = 0.0, dum = 0.0;
+      for (int i = 0; i < GC_TAPS; ++i) {
+        const int64_t tau = t + (GC_TAPS - 1) - i;
+        if (tau >= T) continue;
+        du += cw[(int64_t)i * d + j] * dc[tau * d + j];
+        dum += fabs(cw[(int64_t)i * d + j]) * dcm[tau * d + j];
+      }
+      dv[t * d + j] = du; /* temporarily hold du */
+      if (magv) magv[t * d + j] = dum;
+      s1 += du * wv[j] * vh[j];
+      s1m += dum * fabs(wv[j] * vh[j]);
+      dwv[j] += du * vh[j] * rv;
+      if (mdwv) mdwv[j] += dum * fabs(vh[j] * rv);
+    }
+    /* dvhat and dalpha */
+    double dal = 0.0, dalm = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+      const double du = dv[t * d + j];
+      const double dvh = dY[t * d + j] + rv * (wv[j] * du - vh[j] * rv * rv * s1 / (double)d);
+      const double dvhm = fabs(dY[t * d + j]) +
+                          rv * (fabs(wv[j]) * (magv ? magv[t * d + j] : fabs(du)) + fabs(vh[j]) * rv * rv * s1m / (double)d);
+      dv[t * d + j] = dvh; /* hold dvhat */
+      if (magv) magv[t * d + j] = dvhm;
+      dal += dvh * vt[j];
+      dalm += dvhm * fabs(vt[j]);
+    }
+    const double ds = dal * a * (1.0 - a), dsm = dalm * a * (1.0 - a);
+    double p = 0.0, pm = 0.0; /* sum_j H k w_h^2 */
+    for (int64_t j = 0; j < d; ++j) {
+      p += Ht[j] * kt[j] * wh[j] * wh[j];
+      pm += fabs(Ht[j] * kt[j]) * wh[j] * wh[j];
+    }
+    const double s2 = ds / sd * rk * p, s3 = ds / sd * rh * p; /* <dh^ w_h, H>, <dk^ w_h, k> */
+    const double s2m = dsm / sd * rk * pm, s3m = dsm / sd * rh * pm;
+    for (int64_t j = 0; j < d; ++j) {
+      const double hh = Ht[j] * rh * wh[j], kh = kt[j] * rk * wh[j];
+      const double dhh = ds * kh / sd, dkh = ds * hh / sd;
+      dH[t * d + j] = rh * (wh[j] * dhh - Ht[j] * rh * rh * s2 / (double)d);
+      dk[t * d + j] = rk * (wh[j] * dkh - kt[j] * rk * rk * s3 / (double)d);
+      dwh[j] += dhh * Ht[j] * rh + dkh * kt[j] * rk;
+      if (magH) magH[t * d + j] = rh * (fabs(wh[j]) * dsm * fabs(kh) / sd + fabs(Ht[j]) * rh * rh * s2m / (double)d);
+      if (magk) magk[t * d + j] = rk * (fabs(wh[j]) * dsm * fabs(hh) / sd + fabs(kt[j]) * rk * rk * s3m / (double)d);
+      if (mdwh) mdwh[j] += dsm * (fabs(kh * Ht[j] * rh) + fabs(hh * kt[j] * rk)) / sd;
+    }
+    for (int64_t j = 0; j < d; ++j) {
+      if (magv) magv[t * d + j] *= a; /* alpha is given (saved), so it adds no error */
+      dv[t * d + j] *= a;
+    }
+  }
+}
+
+/*
+ * Backward, fp64 in and out, from fp64 saved tensors.  dwh, dwv [d] and
+ * dcw [4][d] are overwritten with the sums over all M*T tokens.  The mag*
+ * outputs may be NULL.
+ */
+int engram_oracle_gateconv_bwd_f64(int64_t M, int64_t T, int64_t d, const double *dY, const double *H,
+                                   const double *k, const double *v, const double *wh, const double *wv,
+                                   const double *cw, const double *vhat, const double *alpha, const double *rrh,
+                                   const double *rrk, const double *rrv, double *dH, double *dk, double *dv,
+                                   double *dwh, double *dwv, double *dcw, double *magH, double *magk, double *magv,
+                                   double *mdwh, double *mdwv, double *mdcw) {
+  if (M < 0 || T < 0 || d < 1 || !wh || !wv || !cw || !dwh || !dwv || !dcw) return -1;
+  if (M * T > 0 && (!dY || !H || !k || !v || !vhat || !alpha || !rrh || !rrk || !rrv || !dH || !dk || !dv))
+    return -1;
+  for (int64_t j = 0; j < d; ++j) {
+    dwh[j] = dwv[j] = 0.0;
+    if (mdwh) mdwh[j] = 0.0;
+    if (mdwv) mdwv[j] = 0.0;
+  }
+  for (int64_t q = 0; q < GC_TAPS * d; ++q) {
+    dcw[q] = 0.0;
+    if (mdcw) mdcw[q] = 0.0;
+  }
+  double *scr = (double *)malloc(((size_t)3 * T * d + 1) * sizeof(double));
+  if (!scr) return -2;
+  for (int64_t m = 0; m < M; ++m) {
+    const int64_t o = m * T * d, os = m * T;
+    gateconv_bwd_seq(T, d, dY + o, H + o, k + o, v + o, wh, wv, cw, vhat + o, alpha + os, rrh + os, rrk + os,
+                     rrv + os, dH + o, dk + o, dv + o, dwh, dwv, dcw, magH ? magH + o : NULL, magk ? magk + o : NULL,
+                     magv ? magv + o : NULL, mdwh, mdwv, mdcw, scr);
+  }
+  free(scr);
+  return 0;
+}
+
+/* fp64 -> fp32 (RNE) -> bf16 (RNE), elementwise (R10's rounding chain). */
+int engram_oracle_round_bf16(int64_t count, const double *in, uint16_t *out) {
+  if (count < 0 || (count > 0 && (!in || !out))) return -1;
+  for (int64_t q = 0; q < count; ++q) out[q] = double_to_bf16(in[q]);
+  return 0;
+}

@@ -42,6 +42,21 @@ MUTANTS = [
      "grad_wh[q] = dw[q] * bf16_bits_to_double(wh[q]);"),
     ("fused weight drops a factor", "weight[q] = (float)(bf16_bits_to_double(wh[q]) * bf16_bits_to_double(we[q]));",
      "weight[q] = (float)(bf16_bits_to_double(wh[q]));"),
+    # GateConv
+    ("gateconv taps reversed", "c += cw[(int64_t)i * d + j] * u_scr[tau * d + j];",
+     "c += cw[(int64_t)(GC_TAPS - 1 - i) * d + j] * u_scr[tau * d + j];"),
+    ("gateconv gate without 1/sqrt(d)", "s /= sd; /* G2 */", "/* G2 */"),
+    ("gateconv key normalised with w_v", "const double term = (Ht[j] * rh * wh[j]) * (kt[j] * rk * wh[j]);",
+     "const double term = (Ht[j] * rh * wh[j]) * (kt[j] * rk * wv[j]);"),
+    ("gateconv SiLU derivative wrong", "return s * (1.0 + c * (1.0 - s));", "return s;"),
+    ("gateconv residual dropped", "Y[t * d + j] = silu(c) + vhat[t * d + j]; /* G6 */", "Y[t * d + j] = silu(c); /* G6 */"),
+    ("gateconv backward conv runs causally", "const int64_t tau = t + (GC_TAPS - 1) - i;",
+     "const int64_t tau = t - (GC_TAPS - 1) + i;"),
+    ("gateconv rms_v backward sign", "- vh[j] * rv * rv * s1 / (double)d);", "+ vh[j] * rv * rv * s1 / (double)d);"),
+    ("gateconv dv misses alpha", "      dv[t * d + j] *= a;\n", "\n"),
+    ("gateconv dwh drops the key path", "dwh[j] += dhh * Ht[j] * rh + dkh * kt[j] * rk;", "dwh[j] += dhh * Ht[j] * rh;"),
+    ("gateconv dcw pairs the wrong token", "dcw[(int64_t)i * d + j] += dc[t * d + j] * u[tau * d + j];",
+     "dcw[(int64_t)i * d + j] += dc[t * d + j] * u[t * d + j];"),
 ]
 
 
@@ -56,6 +71,7 @@ def test_pins_reject_mutant(desc, old, new, tmp_path):
                            str(lib), str(mutant), "-lm", "-lpthread"])
     env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_gateconv_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
