@@ -41,6 +41,22 @@ BWD_BYTES_PER_TOKEN = 225_344   # X, KV, saved, grad_out read; grad_x, grad_kv w
 BWD_BYTES_FIXED = 163_840       # weight read, grad_weight written
 
 
+# GateConv ("Engram Operators", TileOPs): M sequences of T tokens, width d
+GC_M, GC_T, GC_D = 4, 4096, 5120
+
+
+def gc_fwd_bytes(M, T, d):
+    """H, k, v read, Y and vhat written (bf16); alpha and rrms_h/k/v written
+    (fp32); rms_w_h, rms_w_v, conv_w read (fp32)."""
+    return M * T * (10 * d + 16) + 6 * d * 4
+
+
+def gc_bwd_bytes(M, T, d):
+    """dY, H, k, v, vhat and the four fp32 scalars read, dH, dk, dv written;
+    the 6d fp32 weights read and their gradients written."""
+    return M * T * (16 * d + 16) + 2 * 6 * d * 4
+
+
 def fwd_bytes(n):
     return FWD_BYTES_PER_TOKEN * n + FWD_BYTES_FIXED
 
@@ -49,10 +65,19 @@ def bwd_bytes(n):
     return BWD_BYTES_PER_TOKEN * n + BWD_BYTES_FIXED
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {  # what decides each recorded kernel's traffic: its code and its launch
+    "fwd": ("engram_device.h", "engram_fwd.hip", "engram_api.cpp"),
+    "fwd_large": ("engram_device.h", "engram_fwd.hip", "engram_api.cpp"),
+    "bwd": ("engram_device.h", "engram_bwd.hip", "engram_api.cpp"),
+    "gc_fwd": ("engram_device.h", "engram_gateconv.hip", "engram_api.cpp"),
+    "gc_bwd": ("engram_device.h", "engram_gateconv.hip", "engram_api.cpp"),
+}
+
+
+def kernel_source_hash(kernel):
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -65,7 +90,7 @@ def recorded_traffic(kernel):
     except (OSError, ValueError):
         return None
     e = rec.get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -109,6 +134,70 @@ def cpu_baseline(seconds=10.0, sample=2048):
                       f"repeated {done // sample}x over {el:.1f} s (fp64, {threads} threads)"}
 
 
+def bench_gateconv(torch, synth, eg, dev, stream, steps, R):
+    """GateConv forward then backward over M x T x d, R rotated buffer sets;
+    HIP events around each call on the launching stream."""
+    M, T, d = GC_M, GC_T, GC_D
+    sets = []
+    for _ in range(R):
+        b = {}
+        for name, tid in (("H", synth.ID_GC_H), ("k", synth.ID_GC_K), ("v", synth.ID_GC_V), ("dY", synth.ID_GC_DY)):
+            b[name] = torch.empty((M, T, d), dtype=torch.bfloat16, device=dev)
+            synth.dev_normal_bf16(b[name], SEED, tid)
+        b["wh"] = torch.from_numpy(synth.normal_f32(d, SEED, synth.ID_GC_WH, 1.0, 0.25)).to(dev)
+        b["wv"] = torch.from_numpy(synth.normal_f32(d, SEED, synth.ID_GC_WV, 1.0, 0.25)).to(dev)
+        b["cw"] = torch.from_numpy(synth.normal_f32(4 * d, SEED, synth.ID_GC_CW, 0.0, 0.5).reshape(4, d)).to(dev)
+        for name in ("Y", "vhat", "dH", "dk", "dv"):
+            b[name] = torch.empty((M, T, d), dtype=torch.bfloat16, device=dev)
+        for name in ("alpha", "rh", "rk", "rv"):
+            b[name] = torch.empty((M, T), dtype=torch.float32, device=dev)
+        for name in ("dwh", "dwv"):
+            b[name] = torch.empty(d, dtype=torch.float32, device=dev)
+        b["dcw"] = torch.empty((4, d), dtype=torch.float32, device=dev)
+        b["ws"] = torch.empty(eg.engram_gateconv_bwd_workspace_bytes(M, T, d), dtype=torch.uint8, device=dev)
+        sets.append(b)
+
+    def fwd(b):
+        eg.engram_gateconv_fwd(b["H"], b["k"], b["v"], b["wh"], b["wv"], b["cw"], b["Y"], b["vhat"], b["alpha"],
+                               b["rh"], b["rk"], b["rv"], stream=stream)
+
+    def bwd(b):
+        eg.engram_gateconv_bwd(b["dY"], b["H"], b["k"], b["v"], b["wh"], b["wv"], b["cw"], b["vhat"], b["alpha"],
+                               b["rh"], b["rk"], b["rv"], b["dH"], b["dk"], b["dv"], b["dwh"], b["dwv"], b["dcw"],
+                               b["ws"], stream=stream)
+
+    for i in range(5):
+        fwd(sets[i % R])
+        bwd(sets[i % R])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        b = sets[i % R]
+        ev[i][0].record(stream)
+        fwd(b)
+        ev[i][1].record(stream)
+        bwd(b)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    f_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    b_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    fb, bb = gc_fwd_bytes(M, T, d), gc_bwd_bytes(M, T, d)
+    f_gbps, b_gbps = fb / (f_ms * 1e-3) / 1e9, bb / (b_ms * 1e-3) / 1e9
+    sets.clear()
+    torch.cuda.empty_cache()
+    return {"workload": f"TileOPs GateConv fwd+bwd, M={M} sequences x T={T} tokens x d={d} (bf16 H/k/v/dY "
+                        f"N(0,1), fp32 rms_w N(1,0.25^2), conv_w N(0,0.5^2), seed {SEED})",
+            "tokens_per_s": round(M * T / ((f_ms + b_ms) * 1e-3), 1),
+            "fwd": {"us": round(f_ms * 1e3, 2), "tensor_gbps": round(f_gbps, 1),
+                    "frac_of_peak": round(f_gbps / PEAK_GBPS, 4), "algorithmic_bytes_per_launch": fb,
+                    "traffic": recorded_traffic("gc_fwd")},
+            "bwd": {"us": round(b_ms * 1e3, 2), "tensor_gbps": round(b_gbps, 1),
+                    "frac_of_peak": round(b_gbps / PEAK_GBPS, 4), "algorithmic_bytes_per_launch": bb,
+                    "traffic": recorded_traffic("gc_bwd"),
+                    "kernels": "gateconv_bwd_kernel + gateconv_reduce_kernel"},
+            "steps": steps, "buffer_sets_rotated": R}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +206,8 @@ def main():
     ap.add_argument("--no-large", action="store_true", help="skip the N=1,048,512 forward")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-gateconv", action="store_true", help="skip the GateConv forward/backward")
+    ap.add_argument("--gateconv-steps", type=int, default=50)
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent input/output sets cycled step by step, so that no step "
                          "finds its data in cache from the previous one")
@@ -251,6 +342,9 @@ def main():
             torch.cuda.empty_cache()
         else:
             res["fwd_large"] = {"skipped": f"needs ~{nl * 173 // 1000 // 1000} GB free device memory"}
+
+    if not args.no_gateconv:
+        res["gateconv"] = bench_gateconv(torch, synth, eg, dev, stream, args.gateconv_steps, R)
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -149,6 +149,47 @@ engram_status engram_fused_weight(const void *wh, const void *we, float *weight,
  */
 size_t engram_gate_bwd_workspace_bytes(int64_t N);
 
+/* ==========================================================================
+ * Engram GateConv ("Engram Operators", TileOPs, GateConv section): the
+ * post-projection part of an Engram layer -- RMSNorm gating, a causal
+ * depthwise conv1d with 4 taps, SiLU and the gated value as residual -- with
+ * the saved tensors of the page's backward (vhat, alpha, rrms_h, rrms_k,
+ * rrms_v).  The page gives no formulas; the readings implemented are:
+ *   h^ = H rrms_h w_h, k^ = k rrms_k w_h, rrms = (mean square + eps)^(-1/2)
+ *   alpha = sigmoid(<h^, k^> / sqrt(d)),  vhat = alpha v
+ *   u = vhat rrms_v w_v,  c_t = sum_{i<4} conv_w[i] u_{t-3+i} (zero history)
+ *   Y = SiLU(c) + vhat
+ * Shapes: H, k, v, Y, vhat, dY, dH, dk, dv [M][T][d] bf16; rms_w_h, rms_w_v
+ * [d] fp32; conv_w [4][d] fp32; alpha, rrms_* [M][T] fp32; the weight
+ * gradients are fp32 and overwritten.  d is a multiple of 512, at most 5120;
+ * M, T >= 1 and M * T <= ENGRAM_GATECONV_ROWS_MAX.  All pointers device, 16-byte aligned, outputs overlapping
+ * nothing; asynchronous on `stream`, no allocation or synchronisation.
+ * ========================================================================== */
+#define ENGRAM_GATECONV_D_MAX 5120
+#define ENGRAM_GATECONV_ROWS_MAX 4194304 /* M * T */
+
+/* Forward; argument order of the page's forward(H, k, v, rms_w_h, rms_w_v,
+ * conv_w), then its returned list [Y, vhat, alpha, rrms_h, rrms_k, rrms_v]. */
+engram_status engram_gateconv_fwd(const void *H, const void *k, const void *v, const float *rms_w_h,
+                                  const float *rms_w_v, const float *conv_w, void *Y, void *vhat, float *alpha,
+                                  float *rrms_h, float *rrms_k, float *rrms_v, int64_t M, int64_t T, int64_t d,
+                                  float eps, void *stream);
+
+/* Backward; argument order of the page's backward forward(dY, H, k, v,
+ * rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k, rrms_v), then its
+ * returned list [dH, dk, dv, drms_w_h, drms_w_v, dconv_w], then scratch of
+ * engram_gateconv_bwd_workspace_bytes(M, T, d) bytes (contents ignored). */
+engram_status engram_gateconv_bwd(const void *dY, const void *H, const void *k, const void *v,
+                                  const float *rms_w_h, const float *rms_w_v, const float *conv_w,
+                                  const void *vhat, const float *alpha, const float *rrms_h, const float *rrms_k,
+                                  const float *rrms_v, void *dH, void *dk, void *dv, float *drms_w_h,
+                                  float *drms_w_v, float *dconv_w, void *workspace, int64_t M, int64_t T,
+                                  int64_t d, void *stream);
+
+/* Scratch bytes of engram_gateconv_bwd (fp32 weight-gradient partials of each
+ * token chunk); 0 for sizes the call would reject. */
+size_t engram_gateconv_bwd_workspace_bytes(int64_t M, int64_t T, int64_t d);
+
 /* Human-readable name of a status code (static storage). */
 const char *engram_status_string(int status);
 

@@ -62,6 +62,12 @@ lib.engram_fused_weight.argtypes = [_P, _P, _P, _P]
 lib.engram_fused_weight.restype = ctypes.c_int
 lib.engram_gate_bwd_workspace_bytes.argtypes = [_I64]
 lib.engram_gate_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.engram_gateconv_fwd.argtypes = [_P] * 12 + [_I64, _I64, _I64, ctypes.c_float, _P]
+lib.engram_gateconv_fwd.restype = ctypes.c_int
+lib.engram_gateconv_bwd.argtypes = [_P] * 19 + [_I64, _I64, _I64, _P]
+lib.engram_gateconv_bwd.restype = ctypes.c_int
+lib.engram_gateconv_bwd_workspace_bytes.argtypes = [_I64, _I64, _I64]
+lib.engram_gateconv_bwd_workspace_bytes.restype = ctypes.c_size_t
 lib.engram_status_string.argtypes = [ctypes.c_int]
 lib.engram_status_string.restype = ctypes.c_char_p
 lib.engram_last_hip_error.argtypes = []
@@ -152,5 +158,36 @@ def engram_fused_weight(wh, we, weight, stream=None) -> None:
     _check(lib.engram_fused_weight(_ptr(wh), _ptr(we), _ptr(weight), _stream(stream, wh)))
 
 
-__all__ = ["engram_gate_bwd_with_norm_weights", "engram_fused_weight", "engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
+GATECONV_D_MAX = 5120
+GATECONV_ROWS_MAX = 4194304
+
+
+def engram_gateconv_bwd_workspace_bytes(M: int, T: int, d: int) -> int:
+    """GateConv backward scratch size in bytes (0 for sizes the call rejects)."""
+    return int(lib.engram_gateconv_bwd_workspace_bytes(M, T, d))
+
+
+def engram_gateconv_fwd(H, k, v, rms_w_h, rms_w_v, conv_w, Y, vhat, alpha, rrms_h, rrms_k, rrms_v, eps=1e-6,
+                        stream=None) -> None:
+    """Enqueue the GateConv forward.  H, k, v, Y, vhat [M,T,d] bf16; rms_w_h,
+    rms_w_v [d] fp32; conv_w [4,d] fp32; alpha, rrms_* [M,T] fp32 (written)."""
+    M, T, d = H.shape
+    _check(lib.engram_gateconv_fwd(_ptr(H), _ptr(k), _ptr(v), _ptr(rms_w_h), _ptr(rms_w_v), _ptr(conv_w), _ptr(Y),
+                                   _ptr(vhat), _ptr(alpha), _ptr(rrms_h), _ptr(rrms_k), _ptr(rrms_v), M, T, d, eps,
+                                   _stream(stream, H)))
+
+
+def engram_gateconv_bwd(dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k, rrms_v, dH, dk, dv,
+                        drms_w_h, drms_w_v, dconv_w, workspace, stream=None) -> None:
+    """Enqueue the GateConv backward from the forward's saved tensors; dH, dk,
+    dv [M,T,d] bf16 and drms_w_h, drms_w_v [d], dconv_w [4,d] fp32 are written
+    in full; workspace holds engram_gateconv_bwd_workspace_bytes(M, T, d) bytes."""
+    M, T, d = H.shape
+    _check(lib.engram_gateconv_bwd(_ptr(dY), _ptr(H), _ptr(k), _ptr(v), _ptr(rms_w_h), _ptr(rms_w_v), _ptr(conv_w),
+                                   _ptr(vhat), _ptr(alpha), _ptr(rrms_h), _ptr(rrms_k), _ptr(rrms_v), _ptr(dH),
+                                   _ptr(dk), _ptr(dv), _ptr(drms_w_h), _ptr(drms_w_v), _ptr(dconv_w),
+                                   _ptr(workspace), M, T, d, _stream(stream, H)))
+
+
+__all__ = ["engram_gateconv_fwd", "engram_gateconv_bwd", "engram_gateconv_bwd_workspace_bytes", "engram_gate_bwd_with_norm_weights", "engram_fused_weight", "engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
            "LIB_PATH"]

@@ -142,11 +142,72 @@ engram_status engram_fused_weight(const void* wh, const void* we, float* weight,
   return launched(engram::launch_fused_weight(wh, we, weight, (hipStream_t)stream));
 }
 
+// ---- GateConv ("Engram Operators", TileOPs, GateConv section) ----
+
+static bool gateconv_dims_ok(int64_t M, int64_t T, int64_t d) {
+  return M >= 1 && T >= 1 && M <= ENGRAM_GATECONV_ROWS_MAX && T <= ENGRAM_GATECONV_ROWS_MAX &&
+         M * T <= ENGRAM_GATECONV_ROWS_MAX && d >= 512 && d <= ENGRAM_GATECONV_D_MAX && d % 512 == 0;
+}
+
+size_t engram_gateconv_bwd_workspace_bytes(int64_t M, int64_t T, int64_t d) {
+  if (!gateconv_dims_ok(M, T, d)) return 0;
+  const int chunk = engram::gateconv_chunk(M, T);
+  return (size_t)engram::gateconv_workgroups(M, T, chunk) * 6 * (size_t)d * sizeof(float);
+}
+
+engram_status engram_gateconv_fwd(const void* H, const void* k, const void* v, const float* rms_w_h,
+                                  const float* rms_w_v, const float* conv_w, void* Y, void* vhat, float* alpha,
+                                  float* rrms_h, float* rrms_k, float* rrms_v, int64_t M, int64_t T, int64_t d,
+                                  float eps, void* stream) {
+  if (!H || !k || !v || !rms_w_h || !rms_w_v || !conv_w || !Y || !vhat || !alpha || !rrms_h || !rrms_k || !rrms_v)
+    return ENGRAM_ERR_NULL;
+  if (!gateconv_dims_ok(M, T, d) || !(eps >= 0.0f) || eps > 1.0f) return ENGRAM_ERR_N_RANGE;
+  const void* f16[] = {H, k, v, rms_w_h, rms_w_v, conv_w, Y, vhat, alpha, rrms_h, rrms_k, rrms_v};
+  for (const void* p : f16)
+    if (!aligned16(p)) return ENGRAM_ERR_ALIGN;
+  const int64_t rows = M * T, tb = rows * d * 2, sb = rows * 4;
+  const Range in[] = {range_of(H, tb), range_of(k, tb), range_of(v, tb), range_of(rms_w_h, d * 4),
+                      range_of(rms_w_v, d * 4), range_of(conv_w, 4 * d * 4)};
+  const Range outs[] = {range_of(Y, tb),      range_of(vhat, tb),   range_of(alpha, sb),
+                        range_of(rrms_h, sb), range_of(rrms_k, sb), range_of(rrms_v, sb)};
+  if (any_overlap(in, 6, outs, 6)) return ENGRAM_ERR_OVERLAP;
+  return launched(engram::launch_gateconv_fwd(H, k, v, rms_w_h, rms_w_v, conv_w, Y, vhat, alpha, rrms_h, rrms_k,
+                                              rrms_v, M, T, d, eps, engram::gateconv_chunk(M, T),
+                                              (hipStream_t)stream));
+}
+
+engram_status engram_gateconv_bwd(const void* dY, const void* H, const void* k, const void* v, const float* rms_w_h,
+                                  const float* rms_w_v, const float* conv_w, const void* vhat, const float* alpha,
+                                  const float* rrms_h, const float* rrms_k, const float* rrms_v, void* dH, void* dk,
+                                  void* dv, float* drms_w_h, float* drms_w_v, float* dconv_w, void* workspace,
+                                  int64_t M, int64_t T, int64_t d, void* stream) {
+  if (!dY || !H || !k || !v || !rms_w_h || !rms_w_v || !conv_w || !vhat || !alpha || !rrms_h || !rrms_k ||
+      !rrms_v || !dH || !dk || !dv || !drms_w_h || !drms_w_v || !dconv_w || !workspace)
+    return ENGRAM_ERR_NULL;
+  if (!gateconv_dims_ok(M, T, d)) return ENGRAM_ERR_N_RANGE;
+  const void* f16[] = {dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k, rrms_v,
+                       dH, dk, dv, drms_w_h, drms_w_v, dconv_w, workspace};
+  for (const void* p : f16)
+    if (!aligned16(p)) return ENGRAM_ERR_ALIGN;
+  const int64_t rows = M * T, tb = rows * d * 2, sb = rows * 4;
+  const Range in[] = {range_of(dY, tb),          range_of(H, tb),           range_of(k, tb),
+                      range_of(v, tb),           range_of(rms_w_h, d * 4),  range_of(rms_w_v, d * 4),
+                      range_of(conv_w, 16 * d),  range_of(vhat, tb),        range_of(alpha, sb),
+                      range_of(rrms_h, sb),      range_of(rrms_k, sb),      range_of(rrms_v, sb)};
+  const Range outs[] = {range_of(dH, tb),          range_of(dk, tb),          range_of(dv, tb),
+                        range_of(drms_w_h, d * 4), range_of(drms_w_v, d * 4), range_of(dconv_w, 16 * d),
+                        range_of(workspace, (int64_t)engram_gateconv_bwd_workspace_bytes(M, T, d))};
+  if (any_overlap(in, 12, outs, 7)) return ENGRAM_ERR_OVERLAP;
+  return launched(engram::launch_gateconv_bwd(dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k,
+                                              rrms_v, dH, dk, dv, drms_w_h, drms_w_v, dconv_w, workspace, M, T, d,
+                                              engram::gateconv_chunk(M, T), (hipStream_t)stream));
+}
+
 const char* engram_status_string(int status) {
   switch (status) {
     case ENGRAM_OK: return "ok";
     case ENGRAM_ERR_NULL: return "a required pointer is NULL";
-    case ENGRAM_ERR_N_RANGE: return "N out of range (forward 1..4194240, backward 64..8192)";
+    case ENGRAM_ERR_N_RANGE: return "size out of range (gate: forward N 1..4194240, backward N <= 8192; GateConv: M, T >= 1, M*T <= 4194304, d a multiple of 512 up to 5120, 0 <= eps <= 1)";
     case ENGRAM_ERR_N_MULT64: return "backward N must be a multiple of 64";
     case ENGRAM_ERR_ALIGN: return "floating tensors and workspace must be 16-byte aligned";
     case ENGRAM_ERR_OVERLAP: return "outputs/workspace overlap an input or each other";

@@ -67,9 +67,9 @@ def _load():
         lib.engram_oracle_fused_weight.restype = ctypes.c_int
         lib.engram_oracle_weight_grads.argtypes = [I64, P, P, P, P, P]
         lib.engram_oracle_weight_grads.restype = ctypes.c_int
-        lib.engram_oracle_gateconv_fwd_f64.argtypes = [I64, I64, I64, ctypes.c_double] + [P] * 13
+        lib.engram_oracle_gateconv_fwd_f64.argtypes = [I64, I64, I64, ctypes.c_double] + [P] * 13 + [ctypes.c_int]
         lib.engram_oracle_gateconv_fwd_f64.restype = ctypes.c_int
-        lib.engram_oracle_gateconv_bwd_f64.argtypes = [I64, I64, I64] + [P] * 24
+        lib.engram_oracle_gateconv_bwd_f64.argtypes = [I64, I64, I64] + [P] * 24 + [ctypes.c_int]
         lib.engram_oracle_gateconv_bwd_f64.restype = ctypes.c_int
         lib.engram_oracle_round_bf16.argtypes = [I64, P, P]
         lib.engram_oracle_round_bf16.restype = ctypes.c_int
@@ -241,7 +241,7 @@ def round_bf16(x64):
     return out
 
 
-def gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=1e-6, mags=False):
+def gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=1e-6, mags=False, threads=None):
     """GateConv forward in fp64.  H, k, v [M,T,d]; wh, wv [d]; cw [4,d].
 
     Returns (Y, vhat, alpha, rrms_h, rrms_k, rrms_v) [+ magY].
@@ -255,13 +255,13 @@ def gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=1e-6, mags=False):
     mY = np.empty_like(H) if mags else None
     rc = _load().engram_oracle_gateconv_fwd_f64(M, T, d, eps, _ptr(H), _ptr(k), _ptr(v), _ptr(wh), _ptr(wv),
                                                 _ptr(cw), _ptr(Y), _ptr(vhat), _ptr(al), _ptr(rh), _ptr(rk),
-                                                _ptr(rv), _ptr(mY))
+                                                _ptr(rv), _ptr(mY), threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle gateconv_fwd_f64 failed: {rc}")
     return (Y, vhat, al, rh, rk, rv) + ((mY,) if mags else ())
 
 
-def gateconv_bwd_f64(dY, H, k, v, wh, wv, cw, vhat, alpha, rrh, rrk, rrv, mags=False):
+def gateconv_bwd_f64(dY, H, k, v, wh, wv, cw, vhat, alpha, rrh, rrk, rrv, mags=False, threads=None):
     """GateConv backward in fp64 from the saved tensors.
 
     Returns (dH, dk, dv, dwh, dwv, dcw) [+ (magH, magk, magv, mdwh, mdwv, mdcw)].
@@ -277,7 +277,7 @@ def gateconv_bwd_f64(dY, H, k, v, wh, wv, cw, vhat, alpha, rrh, rrk, rrv, mags=F
     rc = _load().engram_oracle_gateconv_bwd_f64(M, T, d, _ptr(dY), _ptr(H), _ptr(k), _ptr(v), _ptr(wh), _ptr(wv),
                                                 _ptr(cw), _ptr(vhat), _ptr(alpha), _ptr(rrh), _ptr(rrk), _ptr(rrv),
                                                 _ptr(dH), _ptr(dk), _ptr(dv), _ptr(dwh), _ptr(dwv), _ptr(dcw),
-                                                *[_ptr(x) for x in m])
+                                                *[_ptr(x) for x in m], threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle gateconv_bwd_f64 failed: {rc}")
     return (dH, dk, dv, dwh, dwv, dcw) + (m if mags else ())

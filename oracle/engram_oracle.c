@@ -691,26 +691,88 @@ static void gateconv_fwd_seq(int64_t T, int64_t d, double eps, const double *H, 
   }
 }
 
+/* ---- sequences in parallel: thread i takes the contiguous range i of [0, M) ---- */
+
+typedef struct {
+  void (*fn)(void *ctx, int64_t m0, int64_t m1, int tid);
+  void *ctx;
+  int64_t n;
+  int nthreads, tid;
+} seq_arg;
+
+static void *seq_main(void *p) {
+  seq_arg *a = (seq_arg *)p;
+  const int64_t per = (a->n + a->nthreads - 1) / a->nthreads;
+  int64_t m0 = per * a->tid, m1 = m0 + per;
+  if (m1 > a->n) m1 = a->n;
+  if (m0 < m1) a->fn(a->ctx, m0, m1, a->tid);
+  return NULL;
+}
+
+static int seq_threads(int64_t M, int threads) {
+  if (threads < 1) threads = 1;
+  if (threads > 64) threads = 64;
+  if ((int64_t)threads > M) threads = (int)(M > 0 ? M : 1);
+  return threads;
+}
+
+static void run_sequences(int64_t M, int nthreads, void (*fn)(void *, int64_t, int64_t, int), void *ctx) {
+  pthread_t th[64];
+  seq_arg args[64];
+  int started = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    args[i] = (seq_arg){fn, ctx, M, nthreads, i};
+    if (i == 0) continue;
+    if (pthread_create(&th[i], NULL, seq_main, &args[i]) != 0) break;
+    started = i;
+  }
+  seq_main(&args[0]);
+  for (int i = 1; i <= started; ++i) pthread_join(th[i], NULL);
+  for (int i = started + 1; i < nthreads; ++i) seq_main(&args[i]); /* threads that did not start */
+}
+
+typedef struct {
+  int64_t T, d;
+  double eps;
+  const double *H, *k, *v, *wh, *wv, *cw;
+  double *Y, *vhat, *alpha, *rrh, *rrk, *rrv, *magY;
+  int failed;
+} gc_fwd_ctx;
+
+static void gc_fwd_range(void *p, int64_t m0, int64_t m1, int tid) {
+  gc_fwd_ctx *c = (gc_fwd_ctx *)p;
+  (void)tid;
+  const int64_t T = c->T, d = c->d;
+  double *scr = (double *)malloc(((size_t)2 * T * d + (size_t)T + 1) * sizeof(double));
+  if (!scr) {
+    c->failed = -2;
+    return;
+  }
+  for (int64_t m = m0; m < m1; ++m) {
+    const int64_t o = m * T * d, os = m * T;
+    gateconv_fwd_seq(T, d, c->eps, c->H + o, c->k + o, c->v + o, c->wh, c->wv, c->cw, c->Y + o, c->vhat + o,
+                     c->alpha + os, c->rrh + os, c->rrk + os, c->rrv + os, c->magY ? c->magY + o : NULL, scr,
+                     scr + T * d, scr + 2 * T * d);
+  }
+  free(scr);
+}
+
 /*
- * Forward, fp64 in and out.  Returns 0, or -1 for bad arguments, -2 when out
- * of memory.  magY may be NULL.
+ * Forward, fp64 in and out, sequences spread over `threads` threads (each
+ * sequence is computed by one thread exactly as alone).  Returns 0, or -1 for
+ * bad arguments, -2 when out of memory.  magY may be NULL.
  */
 int engram_oracle_gateconv_fwd_f64(int64_t M, int64_t T, int64_t d, double eps, const double *H, const double *k,
                                    const double *v, const double *wh, const double *wv, const double *cw, double *Y,
                                    double *vhat, double *alpha, double *rrh, double *rrk, double *rrv,
-                                   double *magY) {
+                                   double *magY, int threads) {
   if (M < 0 || T < 0 || d < 1) return -1;
   if (M * T > 0 && (!H || !k || !v || !wh || !wv || !cw || !Y || !vhat || !alpha || !rrh || !rrk || !rrv))
     return -1;
-  double *scr = (double *)malloc(((size_t)2 * T * d + (size_t)T + 1) * sizeof(double));
-  if (!scr) return -2;
-  for (int64_t m = 0; m < M; ++m) {
-    const int64_t o = m * T * d, os = m * T;
-    gateconv_fwd_seq(T, d, eps, H + o, k + o, v + o, wh, wv, cw, Y + o, vhat + o, alpha + os, rrh + os, rrk + os,
-                     rrv + os, magY ? magY + o : NULL, scr, scr + T * d, scr + 2 * T * d);
-  }
-  free(scr);
-  return 0;
+  if (M * T == 0) return 0;
+  gc_fwd_ctx c = {T, d, eps, H, k, v, wh, wv, cw, Y, vhat, alpha, rrh, rrk, rrv, magY, 0};
+  run_sequences(M, seq_threads(M, threads), gc_fwd_range, &c);
+  return c.failed;
 }
 
 /*
@@ -816,39 +878,72 @@ static void gateconv_bwd_seq(int64_t T, int64_t d, const double *dY, const doubl
   }
 }
 
+typedef struct {
+  int64_t T, d;
+  const double *dY, *H, *k, *v, *wh, *wv, *cw, *vhat, *alpha, *rrh, *rrk, *rrv;
+  double *dH, *dk, *dv, *magH, *magk, *magv;
+  double *acc; /* per thread [12][d]: dwh, dwv, dcw (4d), then their magnitudes */
+  int mags, failed;
+} gc_bwd_ctx;
+
+static void gc_bwd_range(void *p, int64_t m0, int64_t m1, int tid) {
+  gc_bwd_ctx *c = (gc_bwd_ctx *)p;
+  const int64_t T = c->T, d = c->d;
+  double *scr = (double *)malloc(((size_t)3 * T * d + 1) * sizeof(double));
+  if (!scr) {
+    c->failed = -2;
+    return;
+  }
+  double *a = c->acc + (int64_t)tid * 12 * d;
+  for (int64_t m = m0; m < m1; ++m) {
+    const int64_t o = m * T * d, os = m * T;
+    gateconv_bwd_seq(T, d, c->dY + o, c->H + o, c->k + o, c->v + o, c->wh, c->wv, c->cw, c->vhat + o,
+                     c->alpha + os, c->rrh + os, c->rrk + os, c->rrv + os, c->dH + o, c->dk + o, c->dv + o, a, a + d,
+                     a + 2 * d, c->magH ? c->magH + o : NULL, c->magk ? c->magk + o : NULL,
+                     c->magv ? c->magv + o : NULL, c->mags ? a + 6 * d : NULL, c->mags ? a + 7 * d : NULL,
+                     c->mags ? a + 8 * d : NULL, scr);
+  }
+  free(scr);
+}
+
 /*
- * Backward, fp64 in and out, from fp64 saved tensors.  dwh, dwv [d] and
- * dcw [4][d] are overwritten with the sums over all M*T tokens.  The mag*
- * outputs may be NULL.
+ * Backward, fp64 in and out, from fp64 saved tensors, sequences spread over
+ * `threads` threads.  dwh, dwv [d] and dcw [4][d] are overwritten with the
+ * sums over all M*T tokens: each thread sums its sequences in order, then the
+ * thread sums are added in thread order.  The mag* outputs may be NULL (the
+ * three weight magnitudes together).
  */
 int engram_oracle_gateconv_bwd_f64(int64_t M, int64_t T, int64_t d, const double *dY, const double *H,
                                    const double *k, const double *v, const double *wh, const double *wv,
                                    const double *cw, const double *vhat, const double *alpha, const double *rrh,
                                    const double *rrk, const double *rrv, double *dH, double *dk, double *dv,
                                    double *dwh, double *dwv, double *dcw, double *magH, double *magk, double *magv,
-                                   double *mdwh, double *mdwv, double *mdcw) {
+                                   double *mdwh, double *mdwv, double *mdcw, int threads) {
   if (M < 0 || T < 0 || d < 1 || !wh || !wv || !cw || !dwh || !dwv || !dcw) return -1;
   if (M * T > 0 && (!dY || !H || !k || !v || !vhat || !alpha || !rrh || !rrk || !rrv || !dH || !dk || !dv))
     return -1;
-  for (int64_t j = 0; j < d; ++j) {
-    dwh[j] = dwv[j] = 0.0;
-    if (mdwh) mdwh[j] = 0.0;
-    if (mdwv) mdwv[j] = 0.0;
+  const int mags = mdwh && mdwv && mdcw;
+  const int nt = seq_threads(M, threads);
+  double *acc = (double *)calloc((size_t)nt * 12 * d, sizeof(double));
+  if (!acc) return -2;
+  gc_bwd_ctx c = {T, d, dY, H, k, v, wh, wv, cw, vhat, alpha, rrh, rrk, rrv, dH, dk, dv, magH, magk, magv, acc,
+                  mags, 0};
+  if (M * T > 0) run_sequences(M, nt, gc_bwd_range, &c);
+  for (int64_t j = 0; j < 6 * d; ++j) {
+    double s = 0.0, sm = 0.0;
+    for (int i = 0; i < nt; ++i) {
+      s += acc[(int64_t)i * 12 * d + j];
+      sm += acc[(int64_t)i * 12 * d + 6 * d + j];
+    }
+    double *dst = j < d ? dwh + j : j < 2 * d ? dwv + (j - d) : dcw + (j - 2 * d);
+    *dst = s;
+    if (mags) {
+      double *mdst = j < d ? mdwh + j : j < 2 * d ? mdwv + (j - d) : mdcw + (j - 2 * d);
+      *mdst = sm;
+    }
   }
-  for (int64_t q = 0; q < GC_TAPS * d; ++q) {
-    dcw[q] = 0.0;
-    if (mdcw) mdcw[q] = 0.0;
-  }
-  double *scr = (double *)malloc(((size_t)3 * T * d + 1) * sizeof(double));
-  if (!scr) return -2;
-  for (int64_t m = 0; m < M; ++m) {
-    const int64_t o = m * T * d, os = m * T;
-    gateconv_bwd_seq(T, d, dY + o, H + o, k + o, v + o, wh, wv, cw, vhat + o, alpha + os, rrh + os, rrk + os,
-                     rrv + os, dH + o, dk + o, dv + o, dwh, dwv, dcw, magH ? magH + o : NULL, magk ? magk + o : NULL,
-                     magv ? magv + o : NULL, mdwh, mdwv, mdcw, scr);
-  }
-  free(scr);
-  return 0;
+  free(acc);
+  return c.failed;
 }
 
 /* fp64 -> fp32 (RNE) -> bf16 (RNE), elementwise (R10's rounding chain). */

@@ -24,6 +24,8 @@ _HOST_LIB = os.path.join(_HERE, "libengram_synth_host.so")
 _DEV_LIB = os.path.join(_HERE, "libengram_synth_dev.so")
 
 ID_X, ID_KV, ID_W, ID_MASK, ID_GRAD, ID_EDGE, ID_ZERO = 1, 2, 3, 4, 5, 6, 7
+# GateConv streams: H, k, v, dY, rms_w_h, rms_w_v, conv_w, edge-row choice
+ID_GC_H, ID_GC_K, ID_GC_V, ID_GC_DY, ID_GC_WH, ID_GC_WV, ID_GC_CW, ID_GC_EDGE = 41, 42, 43, 44, 45, 46, 47, 48
 D = 5120
 S = 4
 
@@ -198,3 +200,35 @@ def dev_mask(t, seed: int, p: float, offset: int = 0, tid: int = ID_MASK) -> Non
                              torch.cuda.current_stream(t.device).cuda_stream)
     if rc != 0:
         raise RuntimeError(f"synth_dev_mask failed: hip error {rc}")
+
+
+def gateconv_inputs(M: int, T: int, d: int, seed: int = 0, edge: bool = False) -> dict:
+    """GateConv inputs: H, k, v, dY [M,T,d] bf16 bits of N(0,1); rms_w_h,
+    rms_w_v [d] fp32 of N(1, 0.25^2); conv_w [4,d] fp32 of N(0, 0.5^2).
+
+    edge=True adds the degenerate rows of the map: a row r with word % 17 == 0
+    gets H = k = 0 (alpha = 1/2 from eps alone), == 1 gets k = H (alpha
+    saturates at 1 in fp32), == 2 gets v = 0 (vhat = 0, rrms_v = eps^-1/2)."""
+    n = M * T * d
+    res = {
+        "H": normal_bf16(n, seed, ID_GC_H).reshape(M, T, d),
+        "k": normal_bf16(n, seed, ID_GC_K).reshape(M, T, d),
+        "v": normal_bf16(n, seed, ID_GC_V).reshape(M, T, d),
+        "dY": normal_bf16(n, seed, ID_GC_DY).reshape(M, T, d),
+        "wh": normal_f32(d, seed, ID_GC_WH, 1.0, 0.25),
+        "wv": normal_f32(d, seed, ID_GC_WV, 1.0, 0.25),
+        "cw": normal_f32(4 * d, seed, ID_GC_CW, 0.0, 0.5).reshape(4, d),
+    }
+    if edge:
+        key = stream_key(seed, ID_GC_EDGE)
+        H, k, v = (res[x].reshape(M * T, d) for x in ("H", "k", "v"))
+        for r in range(M * T):
+            kind = word(key, r) % 17
+            if kind == 0:
+                H[r] = 0
+                k[r] = 0
+            elif kind == 1:
+                k[r] = H[r]
+            elif kind == 2:
+                v[r] = 0
+    return res

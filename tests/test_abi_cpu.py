@@ -245,3 +245,118 @@ def test_fused_weight_validation():
     assert f(wh, we, w + 8, None) == eg.ERR_ALIGN
     assert f(wh, we, wh, None) == eg.ERR_OVERLAP
     assert f(wh, we, we + 1024, None) == eg.ERR_OVERLAP
+
+
+# ---------------- GateConv ----------------
+
+def gc_chunk(rows):
+    return min(max(-(-rows // 256), 32), 512)
+
+
+@pytest.mark.parametrize("M,T,d", [(1, 1, 512), (2, 37, 5120), (4, 2048, 5120), (8, 4096, 5120), (1, 4194304, 512),
+                                   (0, 4, 512), (1, 0, 512), (1, 1, 0), (1, 1, 640), (1, 1, 5632), (2, 2097153, 512)])
+def test_gateconv_workspace_formula(M, T, d):
+    rows = M * T
+    ok = M >= 1 and T >= 1 and rows <= 4194304 and d >= 512 and d % 512 == 0 and d <= 5120
+    want = -(-rows // gc_chunk(rows)) * 6 * d * 4 if ok else 0
+    assert eg.engram_gateconv_bwd_workspace_bytes(M, T, d) == want
+
+
+def gc_fwd_layout(M, T, d):
+    tb, sb = M * T * d * 2, M * T * 4
+    a, p = {}, BASE
+    for name, size in (("H", tb), ("k", tb), ("v", tb), ("wh", 4 * d), ("wv", 4 * d), ("cw", 16 * d), ("Y", tb),
+                       ("vhat", tb), ("alpha", sb), ("rh", sb), ("rk", sb), ("rv", sb)):
+        a[name] = p
+        p += size + 4096
+    return a
+
+
+def call_gc_fwd(a, M, T, d, eps=1e-6):
+    return eg.lib.engram_gateconv_fwd(a["H"], a["k"], a["v"], a["wh"], a["wv"], a["cw"], a["Y"], a["vhat"],
+                                      a["alpha"], a["rh"], a["rk"], a["rv"], M, T, d, eps, None)
+
+
+GC_FWD_FIELDS = ["H", "k", "v", "wh", "wv", "cw", "Y", "vhat", "alpha", "rh", "rk", "rv"]
+
+
+@pytest.mark.parametrize("field", GC_FWD_FIELDS)
+def test_gateconv_fwd_rejects_null(field):
+    a = gc_fwd_layout(2, 8, 512)
+    a[field] = None
+    assert call_gc_fwd(a, 2, 8, 512) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("field", GC_FWD_FIELDS)
+def test_gateconv_fwd_rejects_misaligned(field):
+    a = gc_fwd_layout(2, 8, 512)
+    a[field] += 4
+    assert call_gc_fwd(a, 2, 8, 512) == eg.ERR_ALIGN
+
+
+@pytest.mark.parametrize("M,T,d,eps", [(0, 8, 512, 1e-6), (2, 0, 512, 1e-6), (-1, 8, 512, 1e-6), (2, 8, 256, 1e-6),
+                                       (2, 8, 1000, 1e-6), (2, 8, 5632, 1e-6), (4097, 1024, 512, 1e-6),
+                                       (2, 8, 512, -1e-6), (2, 8, 512, float("nan")), (2, 8, 512, 2.0)])
+def test_gateconv_fwd_rejects_bad_sizes(M, T, d, eps):
+    assert call_gc_fwd(gc_fwd_layout(2, 8, 512), M, T, d, eps) == eg.ERR_N_RANGE
+
+
+@pytest.mark.parametrize("out,other", [("Y", "H"), ("vhat", "v"), ("alpha", "wh"), ("rv", "cw"), ("Y", "vhat"),
+                                       ("rh", "rk"), ("alpha", "Y")])
+def test_gateconv_fwd_rejects_overlap(out, other):
+    a = gc_fwd_layout(2, 8, 512)
+    a[out] = a[other]
+    assert call_gc_fwd(a, 2, 8, 512) == eg.ERR_OVERLAP
+
+
+def gc_bwd_layout(M, T, d):
+    tb, sb = M * T * d * 2, M * T * 4
+    a, p = {}, BASE
+    for name, size in (("dY", tb), ("H", tb), ("k", tb), ("v", tb), ("wh", 4 * d), ("wv", 4 * d), ("cw", 16 * d),
+                       ("vhat", tb), ("alpha", sb), ("rh", sb), ("rk", sb), ("rv", sb), ("dH", tb), ("dk", tb),
+                       ("dv", tb), ("dwh", 4 * d), ("dwv", 4 * d), ("dcw", 16 * d),
+                       ("ws", eg.engram_gateconv_bwd_workspace_bytes(M, T, d))):
+        a[name] = p
+        p += size + 4096
+    return a
+
+
+GC_BWD_FIELDS = ["dY", "H", "k", "v", "wh", "wv", "cw", "vhat", "alpha", "rh", "rk", "rv", "dH", "dk", "dv", "dwh",
+                 "dwv", "dcw", "ws"]
+
+
+def call_gc_bwd(a, M, T, d):
+    return eg.lib.engram_gateconv_bwd(*[a[f] for f in GC_BWD_FIELDS], M, T, d, None)
+
+
+@pytest.mark.parametrize("field", GC_BWD_FIELDS)
+def test_gateconv_bwd_rejects_null(field):
+    a = gc_bwd_layout(2, 40, 1024)
+    a[field] = None
+    assert call_gc_bwd(a, 2, 40, 1024) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("field", GC_BWD_FIELDS)
+def test_gateconv_bwd_rejects_misaligned(field):
+    a = gc_bwd_layout(2, 40, 1024)
+    a[field] += 8
+    assert call_gc_bwd(a, 2, 40, 1024) == eg.ERR_ALIGN
+
+
+@pytest.mark.parametrize("M,T,d", [(0, 40, 1024), (2, 0, 1024), (2, 40, 1000), (2, 40, 6144), (5000, 1000, 512)])
+def test_gateconv_bwd_rejects_bad_sizes(M, T, d):
+    assert call_gc_bwd(gc_bwd_layout(2, 40, 1024), M, T, d) == eg.ERR_N_RANGE
+
+
+@pytest.mark.parametrize("out,other", [("dH", "H"), ("dk", "dY"), ("dv", "vhat"), ("dwh", "wh"), ("dcw", "cw"),
+                                       ("ws", "alpha"), ("dH", "dk"), ("dwv", "ws"), ("ws", "dv")])
+def test_gateconv_bwd_rejects_overlap(out, other):
+    a = gc_bwd_layout(2, 40, 1024)
+    a[out] = a[other]
+    assert call_gc_bwd(a, 2, 40, 1024) == eg.ERR_OVERLAP
+
+
+def test_gateconv_bwd_workspace_tail_overlap():
+    a = gc_bwd_layout(2, 40, 1024)
+    a["dcw"] = a["ws"] + eg.engram_gateconv_bwd_workspace_bytes(2, 40, 1024) - 16
+    assert call_gc_bwd(a, 2, 40, 1024) == eg.ERR_OVERLAP
