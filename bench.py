@@ -194,7 +194,7 @@ def bench_gateconv(torch, synth, eg, dev, stream, steps, R):
             "bwd": {"us": round(b_ms * 1e3, 2), "tensor_gbps": round(b_gbps, 1),
                     "frac_of_peak": round(b_gbps / PEAK_GBPS, 4), "algorithmic_bytes_per_launch": bb,
                     "traffic": recorded_traffic("gc_bwd"),
-                    "kernels": "gateconv_bwd_kernel + gateconv_reduce_kernel"},
+                    "kernels": "gateconv_bwd_conv_kernel + gateconv_bwd_hk_kernel + gateconv_reduce_kernel"},
             "steps": steps, "buffer_sets_rotated": R}
 
 

@@ -21,10 +21,11 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
 // Enqueue weight = float(wh) * float(we) for [4][5120] bf16 inputs.
 hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hipStream_t stream);
 
-// GateConv: tokens per workgroup chunk (a function of M*T only), the number of
+// GateConv: rows per workgroup chunk (a function of M*T and d only), the number of
 // workgroups, and the launchers (forward; backward main + weight-gradient reduce).
-int gateconv_chunk(int64_t M, int64_t T);
+int gateconv_chunk(int64_t M, int64_t T, int64_t d);
 int64_t gateconv_workgroups(int64_t M, int64_t T, int chunk);
+size_t gateconv_bwd_workspace(int64_t M, int64_t T, int64_t d, int chunk);
 hipError_t launch_gateconv_fwd(const void* H, const void* K, const void* V, const float* wh, const float* wv,
                                const float* cw, void* Y, void* vhat, float* alpha, float* rrh, float* rrk, float* rrv,
                                int64_t M, int64_t T, int64_t d, float eps, int chunk, hipStream_t stream);

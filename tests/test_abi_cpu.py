@@ -249,8 +249,10 @@ def test_fused_weight_validation():
 
 # ---------------- GateConv ----------------
 
-def gc_chunk(rows):
-    return min(max(-(-rows // 256), 32), 512)
+def gc_chunk(rows, d):
+    nw = d // 512
+    target = 256 * (1 if nw >= 12 else 12 // nw)
+    return min(max(-(-rows // target), 32), 512)
 
 
 @pytest.mark.parametrize("M,T,d", [(1, 1, 512), (2, 37, 5120), (4, 2048, 5120), (8, 4096, 5120), (1, 4194304, 512),
@@ -258,7 +260,7 @@ def gc_chunk(rows):
 def test_gateconv_workspace_formula(M, T, d):
     rows = M * T
     ok = M >= 1 and T >= 1 and rows <= 4194304 and d >= 512 and d % 512 == 0 and d <= 5120
-    want = -(-rows // gc_chunk(rows)) * 6 * d * 4 if ok else 0
+    want = (-(-rows // gc_chunk(rows, d)) * 6 * d * 4 + 4 * rows) if ok else 0
     assert eg.engram_gateconv_bwd_workspace_bytes(M, T, d) == want
 
 
