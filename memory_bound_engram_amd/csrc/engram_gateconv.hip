@@ -60,9 +60,6 @@ __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return __builtin_nonte
 __device__ __forceinline__ u32x2 ld8_keep(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p)); }
 
-// Columns of quad q (q = 0, 1) of thread j, for a row of width d.
-__device__ __forceinline__ int quad_col(int j, int q, int d) { return 4 * (j + q * (d / kCols)); }
-
 // Sum NV (<= 4) values over the NW waves of the workgroup: DPP inside each
 // wave (sum in lane 63), wave partials through LDS, then lanes 0..NW-1 of
 // every wave add them with a 16-lane DPP butterfly and lane 0's sum is
@@ -376,6 +373,15 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_n(min(tau + 1, re - 1));
+    u32x2 fv[2], fg[2];  // the finished row's vhat and dY, read three steps ago: from L2
+    {
+      const int tr = max(t, r0);
+      const uint16_t *pa = vhat + (int64_t)tr * d, *pb = dY + (int64_t)tr * d;
+      fv[0] = ld8(pa + c0);
+      fv[1] = ld8(pa + c1);
+      fg[0] = ld8(pb + c0);
+      fg[1] = ld8(pb + c1);
+    }
     if (tpos == 0) {  // a sequence start: no u history
 #pragma unroll
       for (int i = 0; i < kTaps; ++i)
@@ -383,7 +389,6 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         for (int e = 0; e < kCols; ++e) uh[i][e] = 0.f;
     }
     const float rvn = tau < re ? rrv[tau] : 0.f;  // u = 0 past the rows this chunk needs
-    const float ins = tau < r1 ? 1.0f : 0.0f;     // dc of rows past the chunk enter no gradient
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int cq = q ? c1 : c0;
@@ -411,11 +416,12 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
           const float sg = sigmoidf_(c);
           const float dc = gn[x] * (sg * fmaf(c, 1.0f - sg, 1.0f));
           dch[k0][x] = dc;
-          const float dci = dc * ins;
-          acw[0][x] = fmaf(dci, uh[k1][x], acw[0][x]);
-          acw[1][x] = fmaf(dci, uh[k2][x], acw[1][x]);
-          g2[e] = fmaf(dci, uh[k3][x], g2[e]);
-          g3[e] = fmaf(dci, uh[k0][x], g3[e]);
+          if (tau < r1) {
+            acw[0][x] = fmaf(dc, uh[k1][x], acw[0][x]);
+            acw[1][x] = fmaf(dc, uh[k2][x], acw[1][x]);
+            g2[e] = fmaf(dc, uh[k3][x], g2[e]);
+            g3[e] = fmaf(dc, uh[k0][x], g3[e]);
+          }
         }
         *reinterpret_cast<f32x4*>(lacw + cq) = g2;
         *reinterpret_cast<f32x4*>(lacw + d + cq) = g3;
@@ -438,18 +444,14 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
       const int ahead = T - 1 - t % T;  // rows after t in its sequence
       const float a = alpha[t], rv = rrv[t];
       float vh[kCols], gy[kCols];
-      {  // the finished row's vhat and dY, read three steps ago: from L2
-        const uint16_t *pa = vhat + (int64_t)t * d, *pb = dY + (int64_t)t * d;
-        unpack4(ld8(pa + c0), vh);
-        unpack4(ld8(pa + c1), vh + 4);
-        unpack4(ld8(pb + c0), gy);
-        unpack4(ld8(pb + c1), gy + 4);
-      }
+      unpack4(fv[0], vh);
+      unpack4(fv[1], vh + 4);
+      unpack4(fg[0], gy);
+      unpack4(fg[1], gy + 4);
       // du_t = sum_i conv_w[i] dc_{t+3-i}; dc of rows past the end of t's
       // sequence count as 0 (they belong to the next sequence).  With
       // A = dY + rrms_v w_v du, dvhat = A - rrms_v c1 vhat (c1 = rrms_v^2 S1 / d):
       //   S1 = sum du w_v vhat,  dalpha = sum A v - rrms_v c1 sum vhat v
-      const float m1 = ahead >= 1 ? 1.0f : 0.0f, m2 = ahead >= 2 ? 1.0f : 0.0f, m3 = ahead >= 3 ? 1.0f : 0.0f;
       float s[3];
       float A[kCols];
 #pragma unroll
@@ -464,9 +466,14 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         for (int e = 0; e < 4; ++e) {
           const int x = 4 * q + e;
           float dd = w3[e] * dch[k1][x];
-          dd = fmaf(w2[e], m1 * dch[k2][x], dd);
-          dd = fmaf(w1[e], m2 * dch[k3][x], dd);
-          dd = fmaf(w0[e], m3 * dch[k0][x], dd);
+          if (ahead >= 3) {
+            dd = fmaf(w2[e], dch[k2][x], dd);
+            dd = fmaf(w1[e], dch[k3][x], dd);
+            dd = fmaf(w0[e], dch[k0][x], dd);
+          } else {
+            if (ahead >= 1) dd = fmaf(w2[e], dch[k2][x], dd);
+            if (ahead >= 2) dd = fmaf(w1[e], dch[k3][x], dd);
+          }
           const float dw = dd * wvq[e];
           A[x] = fmaf(rv, dw, gy[x]);
           const float p0 = dw * vh[x], p1 = A[x] * v[x], p2 = vh[x] * v[x];
