@@ -220,3 +220,48 @@ def test_gateconv_full_size(gpu):
     saved = rounded_saved(ref)
     del ref
     check_bwd(run_bwd(inp, saved, gpu), oracle_bwd(inp, saved))
+
+
+def test_gateconv_graph_capture_replays_match_eager(gpu):
+    """Forward + backward (four kernels) captured once in a HIP graph and
+    replayed four times, with outputs and workspace poisoned and unrelated
+    eager work between replays; every replay equals the eager result."""
+    import torch
+    import memory_bound_engram_amd as eg
+    from gpu_util import poison
+    M, T, d = 2, 150, 2048
+    inp = synth.gateconv_inputs(M, T, d, seed=21)
+    args = {x: dev(inp[x], gpu) for x in inp}
+    outs = {x: torch.empty((M, T, d), dtype=torch.bfloat16, device=gpu) for x in ("Y", "vhat", "dH", "dk", "dv")}
+    outs.update({x: torch.empty((M, T), dtype=torch.float32, device=gpu) for x in ("alpha", "rh", "rk", "rv")})
+    outs.update({"dwh": torch.empty(d, dtype=torch.float32, device=gpu),
+                 "dwv": torch.empty(d, dtype=torch.float32, device=gpu),
+                 "dcw": torch.empty((4, d), dtype=torch.float32, device=gpu)})
+    ws = torch.empty(eg.engram_gateconv_bwd_workspace_bytes(M, T, d), dtype=torch.uint8, device=gpu)
+    o = outs
+
+    def step():
+        eg.engram_gateconv_fwd(args["H"], args["k"], args["v"], args["wh"], args["wv"], args["cw"], o["Y"],
+                               o["vhat"], o["alpha"], o["rh"], o["rk"], o["rv"])
+        eg.engram_gateconv_bwd(args["dY"], args["H"], args["k"], args["v"], args["wh"], args["wv"], args["cw"],
+                               o["vhat"], o["alpha"], o["rh"], o["rk"], o["rv"], o["dH"], o["dk"], o["dv"], o["dwh"],
+                               o["dwv"], o["dcw"], ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {x: t.clone() for x, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for t in list(outs.values()) + [ws]:
+            poison(t)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for x, t in outs.items():
+            assert torch.equal(ref[x].view(torch.uint8), t.view(torch.uint8)), f"replay {r}: {x} differs"
+        torch.ones(1 << 20, device=gpu).cumsum(0)  # unrelated eager work between replays
