@@ -33,7 +33,7 @@
 // vectors over its 32 tokens in VGPRs; the two token slots are added in slot
 // order at the end.
 // Kernel 2 (reduce): grad_weight[s][j] = sum over rows of the partials, in a
-// fixed order (8 contiguous row chunks summed sequentially, then the chunk
+// fixed order (32 contiguous row chunks summed sequentially, then the chunk
 // sums added in chunk order), so the result is bitwise reproducible.  When
 // the source norm weights wh, we (weight = wh * we) are given, the same
 // kernel also writes their product-rule gradients grad_wh = grad_weight * we
@@ -214,8 +214,8 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads) prow[j] = comb[j];
 }
 
-constexpr int kReduceChunks = 8;                         // row chunks per column group
-constexpr int kReduceGroups = 32;                        // float4 column groups per workgroup
+constexpr int kReduceChunks = 32;                        // row chunks per column group
+constexpr int kReduceGroups = 8;                         // float4 column groups per workgroup
 constexpr int kReduceThreads = kReduceChunks * kReduceGroups;  // 256
 constexpr int kReduceCols4 = kStreams * kHidden / 4;     // 5120 float4 columns
 
@@ -224,6 +224,8 @@ engram_bwd_reduce_kernel(const float* __restrict__ partial, float* __restrict__ 
                          const uint16_t* __restrict__ wh, const uint16_t* __restrict__ we,
                          float* __restrict__ gwh, float* __restrict__ gwe) {
   __shared__ f32x4 part[kReduceChunks][kReduceGroups];
+  // 640 workgroups of 8 column groups x 32 row chunks (enough waves to keep
+  // the partial rows streaming); a wave reads 8 rows of 128 contiguous bytes
   const int g = threadIdx.x % kReduceGroups;
   const int q = threadIdx.x / kReduceGroups;
   const int col4 = blockIdx.x * kReduceGroups + g;  // grid covers exactly kReduceCols4

@@ -654,25 +654,27 @@ gateconv_bwd_hk_kernel(const uint16_t* __restrict__ H, const uint16_t* __restric
   store_cols<MP>(partial + (int64_t)blockIdx.x * 6 * d, j, awh);
 }
 
-// out[c] = sum over nwg rows of partial[row][c], c < 6d: 8 contiguous row chunks
-// summed sequentially, then the chunk sums in chunk order (fixed for given nwg).
-__global__ void __launch_bounds__(256)
+// out[c] = sum over nwg rows of partial[row][c], c < 6d: 32 contiguous row
+// chunks summed sequentially, then the chunk sums in chunk order (fixed for a
+// given nwg).  Workgroup: 8 float4 column groups x 32 row chunks.
+constexpr int kRedChunks = 32, kRedGroups = 8;
+
+__global__ void __launch_bounds__(kRedChunks * kRedGroups)
 gateconv_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dwh, float* __restrict__ dwv,
                        float* __restrict__ dcw, int nwg, int d) {
-  __shared__ f32x4 part[8][32];
-  const int g = threadIdx.x % 32, q = threadIdx.x / 32;
-  const int c4 = blockIdx.x * 32 + g;  // float4 column of the 6d-wide rows
+  __shared__ f32x4 part[kRedChunks][kRedGroups];
+  const int g = threadIdx.x % kRedGroups, q = threadIdx.x / kRedGroups;
+  const int c4 = blockIdx.x * kRedGroups + g;  // float4 column of the 6d-wide rows; the grid covers 6d/4 exactly
   const int ncol4 = 6 * d / 4;
-  const int b0 = (int)((int64_t)nwg * q / 8), b1 = (int)((int64_t)nwg * (q + 1) / 8);
+  const int b0 = (int)((int64_t)nwg * q / kRedChunks), b1 = (int)((int64_t)nwg * (q + 1) / kRedChunks);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if (c4 < ncol4)
-    for (int b = b0; b < b1; ++b) s += reinterpret_cast<const f32x4*>(partial)[(int64_t)b * ncol4 + c4];
+  for (int b = b0; b < b1; ++b) s += reinterpret_cast<const f32x4*>(partial)[(int64_t)b * ncol4 + c4];
   part[q][g] = s;
   __syncthreads();
-  if (q == 0 && c4 < ncol4) {
+  if (q == 0) {
     f32x4 r = part[0][g];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) r += part[k][g];
+    for (int k = 1; k < kRedChunks; ++k) r += part[k][g];
     const int c = 4 * c4;
     float* dst = c < d ? dwh + c : c < 2 * d ? dwv + (c - d) : dcw + (c - 2 * d);
     *reinterpret_cast<f32x4*>(dst) = r;
@@ -768,8 +770,8 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
   const float* cp = partial;
   int nwi = (int)nwg;
   void* a3[] = {&cp, &dwh, &dwv, &dcw, &nwi, &di};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_kernel),
-                         dim3((unsigned)((6 * d / 4 + 31) / 32)), dim3(256), a3, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_kernel), dim3((unsigned)(6 * d / 4 / kRedGroups)),
+                         dim3(kRedChunks * kRedGroups), a3, 0, stream);
 }
 
 }  // namespace engram
