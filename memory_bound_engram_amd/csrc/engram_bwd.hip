@@ -59,8 +59,12 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
                        const float* __restrict__ weight, const float* __restrict__ saved,
                        const uint16_t* __restrict__ gout, uint16_t* __restrict__ dx,
                        uint16_t* __restrict__ dkv, float* __restrict__ partial, int nb) {
-  __shared__ f32x4 wrow[kHidden / 4];       // weight row of stream s (20 KB)
-  __shared__ f32x4 comb[kHidden / 4];       // token-slot combine (20 KB)
+  // weight row of stream s and the token-slot combine (20 KB each), as two
+  // planes: [0][vec] holds columns 8 vec .. 8 vec + 3, [1][vec] the next four,
+  // so the lanes of a wave read 16-byte words 16 bytes apart (no LDS bank
+  // conflicts; a 32-byte lane stride conflicts 2-way)
+  __shared__ f32x4 wrow[2][kRowVecs];
+  __shared__ f32x4 comb[2][kRowVecs];
   __shared__ float red[2][kBwdSlots][2];    // dg partials of the half-row waves
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = wave >> 1, h = wave & 1;
@@ -71,7 +75,7 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   if (b >= nb) return;  // rows are padded to a multiple of 8
 
   for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads)
-    wrow[j] = reinterpret_cast<const f32x4*>(weight + s * kHidden)[j];
+    wrow[j & 1][j >> 1] = reinterpret_cast<const f32x4*>(weight + s * kHidden)[j];
   float acc[kBwdVecs][kVec];
 #pragma unroll
   for (int v = 0; v < kBwdVecs; ++v)
@@ -137,7 +141,7 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
 #pragma unroll
     for (int v = 0; v < kBwdVecs; ++v) {
       const int vec = lane + 64 * (h + 2 * v);
-      const f32x4 w0 = wrow[2 * vec], w1 = wrow[2 * vec + 1];
+      const f32x4 w0 = wrow[0][vec], w1 = wrow[1][vec];
       const float wv[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       u32x4 ox, ok;
 #pragma unroll
@@ -201,17 +205,17 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
         f32x4 a0 = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
         f32x4 a1 = {acc[v][4], acc[v][5], acc[v][6], acc[v][7]};
         if (uu > 0) {
-          a0 += comb[2 * vec];
-          a1 += comb[2 * vec + 1];
+          a0 += comb[0][vec];
+          a1 += comb[1][vec];
         }
-        comb[2 * vec] = a0;
-        comb[2 * vec + 1] = a1;
+        comb[0][vec] = a0;
+        comb[1][vec] = a1;
       }
     }
     __syncthreads();
   }
   f32x4* prow = reinterpret_cast<f32x4*>(partial + b * (kStreams * kHidden) + s * kHidden);
-  for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads) prow[j] = comb[j];
+  for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads) prow[j] = comb[j & 1][j >> 1];
 }
 
 constexpr int kReduceChunks = 32;                        // row chunks per column group

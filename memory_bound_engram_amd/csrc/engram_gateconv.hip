@@ -139,6 +139,41 @@ __device__ __forceinline__ void store_cols(float* base, int j, const float* f) {
     *reinterpret_cast<f32x2*>(base + MP::pair_col(j)) = f32x2{f[8 * MP::NO], f[8 * MP::NO + 1]};
 }
 
+// Per-thread column vectors kept in LDS (weights the registers cannot hold):
+// only thread j reads what thread j wrote, so the layout is free; it is
+// plane-major -- plane p holds element group p of every thread, lane j at
+// 16 j bytes -- so a wave's ds_read_b128 covers 1 KB contiguous without bank
+// conflicts (the column-major layout, lanes 32 bytes apart, conflicts 2-way).
+// Planes: octet o half h (4 floats) is plane 2o + h; the pair is last.
+template <class MP>
+__device__ __forceinline__ void lds_load(const float* base, int j, float* f) {
+#pragma unroll
+  for (int o = 0; o < MP::NO; ++o)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = reinterpret_cast<const f32x4*>(base + (2 * o + h) * 4 * MP::THREADS)[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[8 * o + 4 * h + e] = a[e];
+    }
+  if constexpr (MP::PAIR) {
+    const f32x2 b = reinterpret_cast<const f32x2*>(base + 8 * MP::NO * MP::THREADS)[j];
+    f[8 * MP::NO] = b[0];
+    f[8 * MP::NO + 1] = b[1];
+  }
+}
+
+template <class MP>
+__device__ __forceinline__ void lds_store(float* base, int j, const float* f) {
+#pragma unroll
+  for (int o = 0; o < MP::NO; ++o)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      reinterpret_cast<f32x4*>(base + (2 * o + h) * 4 * MP::THREADS)[j] =
+          f32x4{f[8 * o + 4 * h], f[8 * o + 4 * h + 1], f[8 * o + 4 * h + 2], f[8 * o + 4 * h + 3]};
+  if constexpr (MP::PAIR)
+    reinterpret_cast<f32x2*>(base + 8 * MP::NO * MP::THREADS)[j] = f32x2{f[8 * MP::NO], f[8 * MP::NO + 1]};
+}
+
 // Sum NV (<= 4) values over the NW waves of the workgroup: DPP inside each
 // wave (sum in lane 63), wave partials through LDS, then lanes 0..NW-1 of
 // every wave add them with a 16-lane DPP butterfly and lane 0's sum is
@@ -373,10 +408,15 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
   const int rb = max(r0 - (kTaps - 1), r0 - r0 % T);            // halo rows before, same sequence
   const int re = min(r1 + (kTaps - 1), ((r1 - 1) / T + 1) * T);  // rows after, same sequence
   constexpr float inv_d = 1.0f / (float)d;
-  for (int q = threadIdx.x; q < 5 * d / 4; q += MP::THREADS) {
-    const int e = 4 * q;
-    const float* src = e < d ? wv + e : cw + (e - d);
-    *reinterpret_cast<f32x4*>(lw + e) = *reinterpret_cast<const f32x4*>(src);
+  {  // this thread's w_v and conv_w columns, plane-major (see lds_load)
+    float t[C];
+    load_cols<MP>(wv, j, t);
+    lds_store<MP>(lw, j, t);
+#pragma unroll
+    for (int i = 0; i < kTaps; ++i) {
+      load_cols<MP>(cw + i * d, j, t);
+      lds_store<MP>(lw + (1 + i) * d, j, t);
+    }
   }
 
   float uh[kTaps][C];   // ring of u rows
@@ -389,8 +429,8 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     for (int i = 0; i < kTaps; ++i) uh[i][e] = dch[i][e] = acw[i][e] = 0.f;
   }
   if constexpr (kLdsTaps) {
-    store_cols<MP>(lacw, j, acw[2]);
-    store_cols<MP>(lacw + d, j, acw[3]);
+    lds_store<MP>(lacw, j, acw[2]);
+    lds_store<MP>(lacw + d, j, acw[3]);
   }
 
   Raw<MP> nv, ng;  // slot N: vhat, dY of the newest row
@@ -438,19 +478,19 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     const float rvn = tau < re ? rrv[tau] : 0.f;  // u = 0 past the rows this chunk needs
     {
       float w4[C];
-      load_cols<MP>(lwv, j, w4);
+      lds_load<MP>(lwv, j, w4);
 #pragma unroll
       for (int e = 0; e < C; ++e) uh[k0][e] = (vn[e] * rvn) * w4[e];
     }
     if (tau >= r0 && tau < re) {
       float w0[C], w1[C], w2[C], w3[C], g2[C], g3[C];
-      load_cols<MP>(lcw, j, w0);
-      load_cols<MP>(lcw + d, j, w1);
-      load_cols<MP>(lcw + 2 * d, j, w2);
-      load_cols<MP>(lcw + 3 * d, j, w3);
+      lds_load<MP>(lcw, j, w0);
+      lds_load<MP>(lcw + d, j, w1);
+      lds_load<MP>(lcw + 2 * d, j, w2);
+      lds_load<MP>(lcw + 3 * d, j, w3);
       if constexpr (kLdsTaps) {
-        load_cols<MP>(lacw, j, g2);
-        load_cols<MP>(lacw + d, j, g3);
+        lds_load<MP>(lacw, j, g2);
+        lds_load<MP>(lacw + d, j, g3);
       }
 #pragma unroll
       for (int x = 0; x < C; ++x) {
@@ -474,8 +514,8 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         }
       }
       if constexpr (kLdsTaps) {
-        store_cols<MP>(lacw, j, g2);
-        store_cols<MP>(lacw + d, j, g3);
+        lds_store<MP>(lacw, j, g2);
+        lds_store<MP>(lacw + d, j, g3);
       }
     } else {
 #pragma unroll
@@ -500,11 +540,11 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
       // A = dY + rrms_v w_v du, dvhat = A - rrms_v c1 vhat (c1 = rrms_v^2 S1 / d):
       //   S1 = sum du w_v vhat,  dalpha = sum A v - rrms_v c1 sum vhat v
       float w0[C], w1[C], w2[C], w3[C], wvq[C];
-      load_cols<MP>(lcw, j, w0);
-      load_cols<MP>(lcw + d, j, w1);
-      load_cols<MP>(lcw + 2 * d, j, w2);
-      load_cols<MP>(lcw + 3 * d, j, w3);
-      load_cols<MP>(lwv, j, wvq);
+      lds_load<MP>(lcw, j, w0);
+      lds_load<MP>(lcw + d, j, w1);
+      lds_load<MP>(lcw + 2 * d, j, w2);
+      lds_load<MP>(lcw + 3 * d, j, w3);
+      lds_load<MP>(lwv, j, wvq);
       float s[3];
       float A[C];
 #pragma unroll
@@ -557,9 +597,9 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
   store_cols<MP>(p + 3 * d, j, acw[1]);
   if constexpr (kLdsTaps) {
     float g[C];
-    load_cols<MP>(lacw, j, g);
+    lds_load<MP>(lacw, j, g);
     store_cols<MP>(p + 4 * d, j, g);
-    load_cols<MP>(lacw + d, j, g);
+    lds_load<MP>(lacw + d, j, g);
     store_cols<MP>(p + 5 * d, j, g);
   } else {
     store_cols<MP>(p + 4 * d, j, acw[2]);
