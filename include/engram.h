@@ -39,8 +39,9 @@
  *     as uninitialised on entry and are written in full.  Inputs may alias
  *     each other; outputs and workspace must not overlap any input or each
  *     other (saved-state paragraph).
- *   - The library holds no state between calls and is thread-safe; calls
- *     on different streams are independent.  Results are bitwise
+ *   - The library holds no state between calls beyond per-device caches of
+ *     fixed facts (the CU count), and is thread-safe; calls on different
+ *     streams are independent.  Results are bitwise
  *     reproducible for identical inputs (fixed reduction orders, no atomics).
  */
 #ifndef ENGRAM_H
@@ -57,7 +58,8 @@ extern "C" {
 typedef enum {
   ENGRAM_OK = 0,
   ENGRAM_ERR_NULL = 1,     /* a required pointer is NULL */
-  ENGRAM_ERR_N_RANGE = 2,  /* N outside 1..4194240 (forward) or 1..8192 (backward) */
+  ENGRAM_ERR_N_RANGE = 2,  /* a size out of range: N outside 1..4194240 (forward) or 1..8192
+                              (backward); GateConv M, T, d, eps outside their limits */
   ENGRAM_ERR_N_MULT64 = 3, /* backward N not a multiple of 64 */
   ENGRAM_ERR_ALIGN = 4,    /* a floating tensor or the workspace is not 16-byte aligned */
   ENGRAM_ERR_OVERLAP = 5,  /* an output or the workspace overlaps an input or another output */
