@@ -125,3 +125,44 @@ def test_graph_capture_replays_match_eager(gpu):
         for a, b in zip(ref, (out, saved, gx, gkv, gw)):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {r} differs"
         torch.ones(1 << 20, device=gpu).cumsum(0)  # unrelated eager work between replays
+
+
+def test_graph_replays_config4_loop_1000(gpu):
+    """The 1000-launch loop of N = 8192 with the edge-row recipe and mask 0.3,
+    replayed from a HIP graph: one captured forward + backward, replayed 1000
+    times on one stream; outputs (poisoned before the loop) equal the eager
+    result bit for bit, and a spot check every 250 replays does too."""
+    import torch
+    import memory_bound_engram_amd as eg
+    from gpu_util import alloc_bwd, dev_inputs, poison
+    n = 8192
+    inp = synth.host_inputs(n, seed=0, p=0.3, grad=True, edge=True)
+    d = dev_inputs(inp, gpu)
+    x, kv, w, m, g = d["x"], d["kv"], d["weight"], d["mask"], d["grad_out"]
+    out = torch.empty_like(x)
+    saved = torch.empty((n, 4, 4), dtype=torch.float32, device=gpu)
+    gx, gkv, gw, ws = alloc_bwd(x, kv, n)
+
+    def step():
+        eg.engram_gate_fwd(x, kv, w, m, out, saved, n)
+        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, saved, gx, gkv, gw)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for t in (out, saved, gx, gkv, gw, ws):
+        poison(t)
+    torch.cuda.synchronize()
+    for i in range(1000):
+        graph.replay()
+        if i % 250 == 249:
+            torch.cuda.synchronize()
+            for a, b in zip(ref, (out, saved, gx, gkv, gw)):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {i} differs"
+    torch.cuda.synchronize()
