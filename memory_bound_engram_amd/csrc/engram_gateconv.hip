@@ -453,6 +453,15 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     const int t = tau - (kTaps - 1);
 
     // ---- newest row tau: u_tau, dc_tau and the conv-weight gradient
+    // The finished row's vhat and dY (read three steps ago: from L2) are
+    // requested first: loads complete in order, so waiting for them later
+    // does not also wait for the newest-row loads issued below.
+    Raw<MP> fv, fg;
+    {
+      const int tr = max(t, r0);
+      load_raw<MP, false>(fv, vhat + (int64_t)tr * d, j);
+      load_raw<MP, false>(fg, dY + (int64_t)tr * d, j);
+    }
     float vn[C], gn[C];
     unpack_raw<MP>(nv, vn);
     unpack_raw<MP>(ng, gn);
@@ -463,12 +472,6 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
     issue_n(min(tau + 1, re - 1));
-    Raw<MP> fv, fg;  // the finished row's vhat and dY, read three steps ago: from L2
-    {
-      const int tr = max(t, r0);
-      load_raw<MP, false>(fv, vhat + (int64_t)tr * d, j);
-      load_raw<MP, false>(fg, dY + (int64_t)tr * d, j);
-    }
     if (tpos == 0) {  // a sequence start: no u history
 #pragma unroll
       for (int i = 0; i < kTaps; ++i)
@@ -546,18 +549,27 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
       lds_load<MP>(lcw + 3 * d, j, w3);
       lds_load<MP>(lwv, j, wvq);
       float s[3];
-      float A[C];
+      float A[C], du[C];
+      if (ahead >= 3) {
 #pragma unroll
-      for (int x = 0; x < C; ++x) {
-        float dd = w3[x] * dch[k1][x];
-        if (ahead >= 3) {
+        for (int x = 0; x < C; ++x) {
+          float dd = w3[x] * dch[k1][x];
           dd = fmaf(w2[x], dch[k2][x], dd);
           dd = fmaf(w1[x], dch[k3][x], dd);
-          dd = fmaf(w0[x], dch[k0][x], dd);
-        } else {
+          du[x] = fmaf(w0[x], dch[k0][x], dd);
+        }
+      } else {  // the last rows of a sequence (rare): rows past its end are skipped
+#pragma unroll
+        for (int x = 0; x < C; ++x) {
+          float dd = w3[x] * dch[k1][x];
           if (ahead >= 1) dd = fmaf(w2[x], dch[k2][x], dd);
           if (ahead >= 2) dd = fmaf(w1[x], dch[k3][x], dd);
+          du[x] = dd;
         }
+      }
+#pragma unroll
+      for (int x = 0; x < C; ++x) {
+        const float dd = du[x];
         const float dw = dd * wvq[x];
         A[x] = fmaf(rv, dw, gy[x]);
         const float p0 = dw * vh[x], p1 = A[x] * v[x], p2 = vh[x] * v[x];
