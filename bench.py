@@ -7,6 +7,7 @@ maximum N), mask Bernoulli(0.9), grad_out N(0,1), synthetic seeded inputs
 already resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--rotate R] [--no-large] [--no-cpu]
+  python bench.py --configs [--no-cpu]     # one line per workload configuration 0-4
 
 Consecutive steps use R (default 4) independent sets of inputs and outputs,
 so no step finds its data in the 256 MB cache from the previous one.
@@ -198,6 +199,122 @@ def bench_gateconv(torch, synth, eg, dev, stream, steps, R):
             "steps": steps, "buffer_sets_rotated": R}
 
 
+# The five workload configurations: forward N=64; forward N=8192; forward +
+# backward N=4096; forward N=1,048,512 in one launch; forward + backward at
+# N=8192 with mask Bernoulli(0.3) and the edge-row recipe (5% of rows with X
+# or a key scaled by 1e-12, 10% of dots inside the clamp), 1000 launches.
+CONFIGS = [
+    dict(config=0, op="fwd", tokens=64, mask_p=0.9, edge=False, launches=200),
+    dict(config=1, op="fwd", tokens=8192, mask_p=0.9, edge=False, launches=200),
+    dict(config=2, op="fwd+bwd", tokens=4096, mask_p=0.9, edge=False, launches=200),
+    dict(config=3, op="fwd", tokens=N_LARGE, mask_p=0.9, edge=False, launches=5),
+    dict(config=4, op="fwd+bwd", tokens=8192, mask_p=0.3, edge=True, launches=1000),
+]
+
+
+def oracle_rate(op, n, p, edge, seconds=3.0, sample=2048):
+    """The fp64 oracle on the host cores over the first min(n, sample) tokens
+    of a configuration's workload, repeated for about `seconds`."""
+    import oracle
+    import synth
+    nt = min(n, sample)
+    inp = synth.host_inputs(n, seed=SEED, p=p, nt=nt, grad=op != "fwd", edge=edge)
+    threads = oracle.default_threads()
+    oracle.fwd_bf16(inp["x"][:8], inp["kv"][:8], inp["weight"], inp["mask"][:8], threads=threads)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        _, saved = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=threads)
+        if op != "fwd":
+            oracle.bwd_bf16(inp["x"], inp["kv"], inp["weight"], saved, inp["grad_out"], threads=threads)
+        done += nt
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"tokens_per_s": round(done / el, 1), "cores": threads,
+            "sample": f"{op} on the first {nt} tokens, repeated {done // nt}x over {el:.1f} s (fp64)"}
+
+
+def bench_configs(torch, synth, eg, dev, stream, with_cpu, rotate):
+    """One JSON line per configuration: GPU time per call (HIP events on the
+    launch stream), tokens/s, tensor-byte GB/s and its fraction of 8 TB/s;
+    the oracle's rate on a bounded sample beside it.  Configurations 0-2
+    cycle `rotate` independent buffer sets, as the benchmark line does;
+    configuration 3 has one set (140 GB); configuration 4 repeats its
+    1000 launches on one set, as specified."""
+    for c in CONFIGS:
+        n, op = c["tokens"], c["op"]
+        grad = op != "fwd"
+        R = rotate if c["config"] <= 2 else 1
+        sets = []
+        for _ in range(R):
+            if c["edge"]:
+                h = synth.host_inputs(n, seed=SEED, p=c["mask_p"], grad=grad, edge=True)
+                x = torch.from_numpy(h["x"].view("int16")).view(torch.bfloat16).to(dev)
+                kv = torch.from_numpy(h["kv"].view("int16")).view(torch.bfloat16).to(dev)
+                w = torch.from_numpy(h["weight"]).to(dev)
+                m = torch.from_numpy(h["mask"]).to(dev)
+                g = torch.from_numpy(h["grad_out"].view("int16")).view(torch.bfloat16).to(dev) if grad else None
+                del h
+            else:
+                x = torch.empty((n, 4, 5120), dtype=torch.bfloat16, device=dev)
+                kv = torch.empty((n, 25600), dtype=torch.bfloat16, device=dev)
+                m = torch.empty(n, dtype=torch.uint8, device=dev)
+                synth.dev_normal_bf16(x, SEED, synth.ID_X)
+                synth.dev_normal_bf16(kv, SEED, synth.ID_KV)
+                synth.dev_mask(m, SEED, c["mask_p"])
+                w = torch.from_numpy(synth.normal_f32(4 * 5120, SEED, synth.ID_W, 1.0, 0.1).reshape(4, 5120)).to(dev)
+                g = None
+                if grad:
+                    g = torch.empty((n, 4, 5120), dtype=torch.bfloat16, device=dev)
+                    synth.dev_normal_bf16(g, SEED, synth.ID_GRAD)
+            b = dict(x=x, kv=kv, w=w, m=m, g=g, out=torch.empty_like(x),
+                     saved=torch.empty((n, 4, 4), dtype=torch.float32, device=dev))
+            if grad:
+                b.update(gx=torch.empty_like(x), gkv=torch.empty_like(kv),
+                         gw=torch.empty((4, 5120), dtype=torch.float32, device=dev),
+                         ws=torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev))
+            sets.append(b)
+            x = kv = w = m = g = None
+
+        def call(b):
+            eg.engram_gate_fwd(b["x"], b["kv"], b["w"], b["m"], b["out"], b["saved"], n, stream=stream)
+            if grad:
+                eg.engram_gate_bwd(b["x"], b["kv"], b["w"], b["saved"], b["g"], b["gx"], b["gkv"], b["gw"],
+                                   b["ws"], n, stream=stream)
+
+        for i in range(max(3, R)):
+            call(sets[i % R])
+        torch.cuda.synchronize()
+        K = c["launches"]
+        if K >= 1000:  # one stream, back to back: the loop's time over its launches
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                call(sets[i % R])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / K
+        else:  # median of per-call times
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+            for i, (e0, e1) in enumerate(ev):
+                e0.record(stream)
+                call(sets[i % R])
+                e1.record(stream)
+            torch.cuda.synchronize()
+            us = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[K // 2] * 1e3
+        byt = fwd_bytes(n) + (bwd_bytes(n) if grad else 0)
+        gbps = byt / (us * 1e-6) / 1e9
+        line = {"config": c["config"], "op": op, "tokens": n, "mask_p": c["mask_p"], "edge_rows": c["edge"],
+                "launches": K, "buffer_sets_rotated": R, "us_per_call": round(us, 2),
+                "tokens_per_s": round(n / (us * 1e-6), 1), "tensor_bytes_per_call": byt,
+                "tensor_gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}
+        sets.clear()
+        torch.cuda.empty_cache()
+        if with_cpu:
+            line["oracle"] = oracle_rate(op, n, c["mask_p"], c["edge"])
+        print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +328,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=4,
                     help="independent input/output sets cycled step by step, so that no step "
                          "finds its data in cache from the previous one")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the benchmark line, one line per workload configuration (0-4)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -234,6 +353,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.configs:
+        bench_configs(torch, synth, eg, dev, torch.cuda.current_stream(dev), not args.no_cpu, max(1, args.rotate))
+        return
     n = N_STEP
     R = max(1, args.rotate)
     sets = []

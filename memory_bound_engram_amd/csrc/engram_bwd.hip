@@ -22,15 +22,17 @@
 // tokens in the same order, so the shared value and the grad_out slices they
 // all read are fetched from HBM once (normal loads; streaming hints would
 // evict them before the sibling workgroups arrive).
-// Inside a workgroup: 2 token slots x 2 half-row waves.  Wave (u, h) handles
-// tokens k = u, u + 2, ... of the row and vectors h + 2i (i = 0..4) of the
-// 640 16-byte vectors of a stream row.  The dg partials of the two half-row
+// Inside a workgroup: S token slots x 2 half-row waves.  Wave (u, h) handles
+// tokens k = u, u + S, ... of the row and vectors h + 2i (i = 0..4) of the
+// 640 16-byte vectors of a stream row.  S = 2 (256 threads) when there are at
+// least 512 (row, stream) workgroups, two per CU; below that (N < 8192) S = 4
+// (512 threads), so each CU still runs eight waves.  The dg partials of the two half-row
 // waves of a token meet in LDS (one barrier per pair of tokens).  grad_value
 // for vector pair i (columns of vectors 2i, 2i+1) is written by the stream-i
 // workgroup for i < 4 and, for i = 4, by the stream (k mod 4) workgroup, so
 // every element is written once and the extra grad_out reads stay balanced.
 // The weight row of stream s sits in LDS.  Each wave accumulates a x k for its
-// vectors over its 32 tokens in VGPRs; the two token slots are added in slot
+// vectors over its 64 / S tokens in VGPRs; the token slots are added in slot
 // order at the end.
 // Kernel 2 (reduce): grad_weight[s][j] = sum over rows of the partials, in a
 // fixed order (32 contiguous row chunks summed sequentially, then the chunk
@@ -49,12 +51,10 @@
 
 namespace engram {
 
-constexpr int kBwdSlots = 2;                          // token slots per workgroup
-constexpr int kBwdThreads = 64 * 2 * kBwdSlots;       // 2 half-row waves per slot
 constexpr int kBwdVecs = kRowVecs / 128;              // 5 vectors per lane (half a row)
-constexpr int kTokensPerSlot = kTokensPerPartial / kBwdSlots;
 
-__global__ void __launch_bounds__(kBwdThreads)
+template <int kBwdSlots>
+__global__ void __launch_bounds__(64 * 2 * kBwdSlots)
 engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
                        const float* __restrict__ weight, const float* __restrict__ saved,
                        const uint16_t* __restrict__ gout, uint16_t* __restrict__ dx,
@@ -65,6 +65,8 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   // conflicts; a 32-byte lane stride conflicts 2-way)
   __shared__ f32x4 wrow[2][kRowVecs];
   __shared__ f32x4 comb[2][kRowVecs];
+  constexpr int kBwdThreads = 64 * 2 * kBwdSlots;       // 2 half-row waves per slot
+  constexpr int kTokensPerSlot = kTokensPerPartial / kBwdSlots;
   __shared__ float red[2][kBwdSlots][2];    // dg partials of the half-row waves
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int u = wave >> 1, h = wave & 1;
@@ -298,8 +300,11 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
   int nbv = nb;
   void* args1[] = {&xp, &kvp, &weight, &saved, &gp, &dxp, &dkvp, &partial, &nbv};
   const int grid1 = (nb + 7) / 8 * 8 * kStreams;  // (row, stream) pairs, rows padded to 8
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_main_kernel), dim3(grid1),
-                                 dim3(kBwdThreads), args1, 0, stream);
+  // four token slots when two-slot workgroups would leave CUs with fewer than eight waves
+  const bool four = grid1 < 512;
+  hipError_t e = hipLaunchKernel(four ? reinterpret_cast<const void*>(&engram_bwd_main_kernel<4>)
+                                      : reinterpret_cast<const void*>(&engram_bwd_main_kernel<2>),
+                                 dim3(grid1), dim3(four ? 512 : 256), args1, 0, stream);
   if (e != hipSuccess) return e;
   const float* cpartial = partial;
   const uint16_t* whp = static_cast<const uint16_t*>(wh);
