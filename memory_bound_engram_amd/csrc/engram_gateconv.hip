@@ -15,6 +15,8 @@
 //   with g = ds rrms_h rrms_k / sqrt(d) and P = sum_j H k w_h^2:
 //   dH = g (w_h^2 k - H rrms_h^2 P / d),  dk = g (w_h^2 H - k rrms_k^2 P / d)
 //   dw_h += 2 g w_h H k,  dw_v += du vhat rrms_v
+// (dw_v is formed as sum_i conv_w[i] sum_t dc_t u_{t-3+i} / w_v: the same
+// products, regrouped; see the reduce kernel).
 //
 // Mapping.  A workgroup owns whole token rows and walks a chunk of consecutive
 // rows of the flattened [M*T] token order (a chunk may cross into the next
@@ -37,6 +39,7 @@ namespace {
 
 constexpr int kTaps = 4;
 constexpr int kMaxWaves = 10;
+constexpr int kPartRows = 1 + kTaps;  // weight-gradient partial rows per workgroup: rms_w_h, conv_w taps
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -377,7 +380,8 @@ gateconv_fwd_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__
 // each tensor is still read once and each kernel's per-thread state fits the
 // register file of a CU that holds one row-wide workgroup:
 //   conv kernel: vhat, dY, v -> dv, the per-row ds = dalpha alpha (1 - alpha),
-//                and the conv_w and rms_w_v gradient partials;
+//                and the conv_w gradient partials (against u / w_v, from which
+//                the reduce also forms the rms_w_v gradient);
 //   h/k kernel:  H, k and the per-row scalars -> dH, dk and the rms_w_h partials.
 //
 // Conv kernel.  Row tau = newest row (its vhat and dY give u_tau and dc_tau);
@@ -385,7 +389,8 @@ gateconv_fwd_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__
 // run one step ahead: slot N holds vhat, dY of the next newest row, slot L
 // holds v of the next finished row; the finished row's vhat and dY, read three
 // steps earlier, come from L2.  The step is unrolled by four, so the u and dc
-// histories are rings whose slots have fixed roles in each of the four steps.
+// histories are rings whose slots have fixed roles in each of the four steps;
+// the u ring holds u / w_v = vhat rrms_v.
 // LDS holds w_v and conv_w; with more than eight waves (at most 168 VGPRs a
 // thread) the conv_w tap 2 and 3 gradient accumulators move to LDS too.
 template <class MP>
@@ -419,15 +424,13 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     }
   }
 
-  float uh[kTaps][C];   // ring of u rows
+  float uh[kTaps][C];   // ring of u / w_v rows (vhat rrms_v)
   float dch[kTaps][C];  // ring of dc rows
-  float awv[C], acw[kTaps][C];  // rms_w_v and conv_w gradients (taps 2, 3 unused when in LDS)
+  float acw[kTaps][C];  // conv_w gradients against u / w_v (taps 2, 3 unused when in LDS)
 #pragma unroll
-  for (int e = 0; e < C; ++e) {
-    awv[e] = 0.f;
+  for (int e = 0; e < C; ++e)
 #pragma unroll
     for (int i = 0; i < kTaps; ++i) uh[i][e] = dch[i][e] = acw[i][e] = 0.f;
-  }
   if constexpr (kLdsTaps) {
     lds_store<MP>(lacw, j, acw[2]);
     lds_store<MP>(lacw + d, j, acw[3]);
@@ -479,14 +482,11 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         for (int e = 0; e < C; ++e) uh[i][e] = 0.f;
     }
     const float rvn = tau < re ? rrv[tau] : 0.f;  // u = 0 past the rows this chunk needs
-    {
-      float w4[C];
-      lds_load<MP>(lwv, j, w4);
 #pragma unroll
-      for (int e = 0; e < C; ++e) uh[k0][e] = (vn[e] * rvn) * w4[e];
-    }
+    for (int e = 0; e < C; ++e) uh[k0][e] = vn[e] * rvn;
     if (tau >= r0 && tau < re) {
-      float w0[C], w1[C], w2[C], w3[C], g2[C], g3[C];
+      float w0[C], w1[C], w2[C], w3[C], g2[C], g3[C], w4[C];
+      lds_load<MP>(lwv, j, w4);
       lds_load<MP>(lcw, j, w0);
       lds_load<MP>(lcw + d, j, w1);
       lds_load<MP>(lcw + 2 * d, j, w2);
@@ -500,7 +500,7 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         float c = w0[x] * uh[k1][x];
         c = fmaf(w1[x], uh[k2][x], c);
         c = fmaf(w2[x], uh[k3][x], c);
-        c = fmaf(w3[x], uh[k0][x], c);
+        c = fmaf(w3[x], uh[k0][x], c) * w4[x];
         const float sg = sigmoidf_(c);
         const float dc = gn[x] * (sg * fmaf(c, 1.0f - sg, 1.0f));
         dch[k0][x] = dc;
@@ -576,7 +576,6 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
         s[0] = x == 0 ? p0 : s[0] + p0;
         s[1] = x == 0 ? p1 : s[1] + p1;
         s[2] = x == 0 ? p2 : s[2] + p2;
-        awv[x] = fmaf(dd, vh[x] * rv, awv[x]);
       }
       block_sum<3, MP::NW>(s, red, buf);
       const float rc = rv * ((rv * rv) * (s[0] * inv_d));  // rrms_v c1
@@ -602,20 +601,19 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
   if (tau + 1 < end) step(tau + 1, I1{});
   if (tau + 2 < end) step(tau + 2, I2{});
 
-  // this workgroup's partials: rows 1 (rms_w_v) and 2..5 (conv_w) of its [6][d] block
-  float* p = partial + (int64_t)blockIdx.x * 6 * d;
-  store_cols<MP>(p + d, j, awv);
-  store_cols<MP>(p + 2 * d, j, acw[0]);
-  store_cols<MP>(p + 3 * d, j, acw[1]);
+  // this workgroup's partials: rows 1..4 (the conv_w taps, against u / w_v) of its [5][d] block
+  float* p = partial + (int64_t)blockIdx.x * kPartRows * d;
+  store_cols<MP>(p + d, j, acw[0]);
+  store_cols<MP>(p + 2 * d, j, acw[1]);
   if constexpr (kLdsTaps) {
     float g[C];
     lds_load<MP>(lacw, j, g);
-    store_cols<MP>(p + 4 * d, j, g);
+    store_cols<MP>(p + 3 * d, j, g);
     lds_load<MP>(lacw + d, j, g);
-    store_cols<MP>(p + 5 * d, j, g);
+    store_cols<MP>(p + 4 * d, j, g);
   } else {
-    store_cols<MP>(p + 4 * d, j, acw[2]);
-    store_cols<MP>(p + 5 * d, j, acw[3]);
+    store_cols<MP>(p + 3 * d, j, acw[2]);
+    store_cols<MP>(p + 4 * d, j, acw[3]);
   }
 }
 
@@ -702,34 +700,54 @@ gateconv_bwd_hk_kernel(const uint16_t* __restrict__ H, const uint16_t* __restric
   if (r < r1) step(r, sa);
   if (r + 1 < r1) step(r + 1, sb);
 
-  // row 0 (rms_w_h) of this workgroup's [6][d] partial block
-  store_cols<MP>(partial + (int64_t)blockIdx.x * 6 * d, j, awh);
+  // row 0 (rms_w_h) of this workgroup's [5][d] partial block
+  store_cols<MP>(partial + (int64_t)blockIdx.x * kPartRows * d, j, awh);
 }
 
-// out[c] = sum over nwg rows of partial[row][c], c < 6d: 32 contiguous row
-// chunks summed sequentially, then the chunk sums in chunk order (fixed for a
-// given nwg).  Workgroup: 8 float4 column groups x 32 row chunks.
+// Weight gradients from the [nwg][5][d] partials.  Per column x: s_r = sum
+// over the workgroups of partial row r (32 contiguous chunks of workgroups,
+// each summed sequentially, then the chunk sums in chunk order: fixed for a
+// given nwg), then
+//   drms_w_h = s_0,   dconv_w[i] = w_v s_{1+i},   drms_w_v = sum_i conv_w[i] s_{1+i}.
+// The last line is the rms_w_v gradient sum_t du_t u_t / w_v regrouped: with
+// du_t = sum_i conv_w[i] dc_{t+3-i}, both sides add conv_w[i] dc_tau u_t / w_v
+// over the same pairs (t, tau = t + 3 - i) of rows of one sequence.
 constexpr int kRedChunks = 32, kRedGroups = 8;
 
 __global__ void __launch_bounds__(kRedChunks * kRedGroups)
-gateconv_reduce_kernel(const float* __restrict__ partial, float* __restrict__ dwh, float* __restrict__ dwv,
-                       float* __restrict__ dcw, int nwg, int d) {
-  __shared__ f32x4 part[kRedChunks][kRedGroups];
+gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restrict__ wv, const float* __restrict__ cw,
+                       float* __restrict__ dwh, float* __restrict__ dwv, float* __restrict__ dcw, int nwg, int d) {
+  __shared__ f32x4 part[kRedChunks][kPartRows][kRedGroups];
   const int g = threadIdx.x % kRedGroups, q = threadIdx.x / kRedGroups;
-  const int c4 = blockIdx.x * kRedGroups + g;  // float4 column of the 6d-wide rows; the grid covers 6d/4 exactly
-  const int ncol4 = 6 * d / 4;
+  const int c4 = blockIdx.x * kRedGroups + g;  // float4 column; the grid covers d/4 exactly
+  const int ncol4 = d / 4;
   const int b0 = (int)((int64_t)nwg * q / kRedChunks), b1 = (int)((int64_t)nwg * (q + 1) / kRedChunks);
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int b = b0; b < b1; ++b) s += reinterpret_cast<const f32x4*>(partial)[(int64_t)b * ncol4 + c4];
-  part[q][g] = s;
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(partial);
+  f32x4 s[kPartRows];
+#pragma unroll
+  for (int r = 0; r < kPartRows; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = b0; b < b1; ++b)
+#pragma unroll
+    for (int r = 0; r < kPartRows; ++r) s[r] += p4[((int64_t)b * kPartRows + r) * ncol4 + c4];
+#pragma unroll
+  for (int r = 0; r < kPartRows; ++r) part[q][r][g] = s[r];
   __syncthreads();
   if (q == 0) {
-    f32x4 r = part[0][g];
+    f32x4 t[kPartRows];
 #pragma unroll
-    for (int k = 1; k < kRedChunks; ++k) r += part[k][g];
-    const int c = 4 * c4;
-    float* dst = c < d ? dwh + c : c < 2 * d ? dwv + (c - d) : dcw + (c - 2 * d);
-    *reinterpret_cast<f32x4*>(dst) = r;
+    for (int r = 0; r < kPartRows; ++r) {
+      t[r] = part[0][r][g];
+      for (int k = 1; k < kRedChunks; ++k) t[r] += part[k][r][g];
+    }
+    reinterpret_cast<f32x4*>(dwh)[c4] = t[0];
+    const f32x4 w = reinterpret_cast<const f32x4*>(wv)[c4];
+    f32x4 v = reinterpret_cast<const f32x4*>(cw)[c4] * t[1];
+#pragma unroll
+    for (int i = 0; i < kTaps; ++i) {
+      reinterpret_cast<f32x4*>(dcw)[i * ncol4 + c4] = w * t[1 + i];
+      if (i > 0) v += reinterpret_cast<const f32x4*>(cw)[i * ncol4 + c4] * t[1 + i];
+    }
+    reinterpret_cast<f32x4*>(dwv)[c4] = v;
   }
 }
 
@@ -779,8 +797,9 @@ int gateconv_chunk(int64_t M, int64_t T, int64_t d) {
 int64_t gateconv_workgroups(int64_t M, int64_t T, int chunk) { return (M * T + chunk - 1) / chunk; }
 
 size_t gateconv_bwd_workspace(int64_t M, int64_t T, int64_t d, int chunk) {
-  // [nwg][6][d] fp32 weight-gradient partials, then the per-row ds [M*T]
-  return (size_t)gateconv_workgroups(M, T, chunk) * 6 * (size_t)d * sizeof(float) + (size_t)(M * T) * sizeof(float);
+  // [nwg][5][d] fp32 weight-gradient partials, then the per-row ds [M*T]
+  return (size_t)gateconv_workgroups(M, T, chunk) * kPartRows * (size_t)d * sizeof(float) +
+         (size_t)(M * T) * sizeof(float);
 }
 
 hipError_t launch_gateconv_fwd(const void* H, const void* K, const void* V, const float* wh, const float* wv,
@@ -810,7 +829,7 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
   uint16_t *dhp = static_cast<uint16_t*>(dH), *dkp = static_cast<uint16_t*>(dK), *dvp = static_cast<uint16_t*>(dV);
   const int64_t nwg = gateconv_workgroups(M, T, chunk);
   float* partial = static_cast<float*>(workspace);
-  float* ds = partial + nwg * 6 * d;
+  float* ds = partial + nwg * kPartRows * d;
   int rows = (int)(M * T), Ti = (int)T, di = (int)d, ch = chunk;
   void* a1[] = {&gp, &vp, &wv, &cw, &vhp, &alpha, &rrv, &dvp, &ds, &partial, &rows, &Ti, &ch};
   hipError_t e = hipLaunchKernel(kn->conv, dim3((unsigned)nwg), dim3((unsigned)kn->threads), a1, 0, stream);
@@ -821,8 +840,8 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
   if (e != hipSuccess) return e;
   const float* cp = partial;
   int nwi = (int)nwg;
-  void* a3[] = {&cp, &dwh, &dwv, &dcw, &nwi, &di};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_kernel), dim3((unsigned)(6 * d / 4 / kRedGroups)),
+  void* a3[] = {&cp, &wv, &cw, &dwh, &dwv, &dcw, &nwi, &di};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_kernel), dim3((unsigned)(d / 4 / kRedGroups)),
                          dim3(kRedChunks * kRedGroups), a3, 0, stream);
 }
 

@@ -260,7 +260,7 @@ def gc_chunk(rows, d):
 def test_gateconv_workspace_formula(M, T, d):
     rows = M * T
     ok = M >= 1 and T >= 1 and rows <= 4194304 and d >= 512 and d % 512 == 0 and d <= 5120
-    want = (-(-rows // gc_chunk(rows, d)) * 6 * d * 4 + 4 * rows) if ok else 0
+    want = (-(-rows // gc_chunk(rows, d)) * 5 * d * 4 + 4 * rows) if ok else 0
     assert eg.engram_gateconv_bwd_workspace_bytes(M, T, d) == want
 
 
