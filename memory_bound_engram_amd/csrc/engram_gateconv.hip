@@ -705,19 +705,20 @@ gateconv_bwd_hk_kernel(const uint16_t* __restrict__ H, const uint16_t* __restric
 }
 
 // Weight gradients from the [nwg][5][d] partials.  Per column x: s_r = sum
-// over the workgroups of partial row r (32 contiguous chunks of workgroups,
+// over the workgroups of partial row r (64 contiguous chunks of workgroups,
 // each summed sequentially, then the chunk sums in chunk order: fixed for a
 // given nwg), then
 //   drms_w_h = s_0,   dconv_w[i] = w_v s_{1+i},   drms_w_v = sum_i conv_w[i] s_{1+i}.
 // The last line is the rms_w_v gradient sum_t du_t u_t / w_v regrouped: with
 // du_t = sum_i conv_w[i] dc_{t+3-i}, both sides add conv_w[i] dc_tau u_t / w_v
 // over the same pairs (t, tau = t + 3 - i) of rows of one sequence.
-constexpr int kRedChunks = 32, kRedGroups = 8;
+constexpr int kRedChunks = 64, kRedGroups = 8;
 
 __global__ void __launch_bounds__(kRedChunks * kRedGroups)
 gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restrict__ wv, const float* __restrict__ cw,
                        float* __restrict__ dwh, float* __restrict__ dwv, float* __restrict__ dcw, int nwg, int d) {
   __shared__ f32x4 part[kRedChunks][kPartRows][kRedGroups];
+  __shared__ f32x4 tot[kPartRows][kRedGroups];
   const int g = threadIdx.x % kRedGroups, q = threadIdx.x / kRedGroups;
   const int c4 = blockIdx.x * kRedGroups + g;  // float4 column; the grid covers d/4 exactly
   const int ncol4 = d / 4;
@@ -726,26 +727,27 @@ gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restric
   f32x4 s[kPartRows];
 #pragma unroll
   for (int r = 0; r < kPartRows; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
   for (int b = b0; b < b1; ++b)
 #pragma unroll
     for (int r = 0; r < kPartRows; ++r) s[r] += p4[((int64_t)b * kPartRows + r) * ncol4 + c4];
 #pragma unroll
   for (int r = 0; r < kPartRows; ++r) part[q][r][g] = s[r];
   __syncthreads();
+  if (q < kPartRows) {  // row q of this column group: the chunk sums in chunk order
+    f32x4 t = part[0][q][g];
+    for (int k = 1; k < kRedChunks; ++k) t += part[k][q][g];
+    tot[q][g] = t;
+  }
+  __syncthreads();
   if (q == 0) {
-    f32x4 t[kPartRows];
-#pragma unroll
-    for (int r = 0; r < kPartRows; ++r) {
-      t[r] = part[0][r][g];
-      for (int k = 1; k < kRedChunks; ++k) t[r] += part[k][r][g];
-    }
-    reinterpret_cast<f32x4*>(dwh)[c4] = t[0];
+    reinterpret_cast<f32x4*>(dwh)[c4] = tot[0][g];
     const f32x4 w = reinterpret_cast<const f32x4*>(wv)[c4];
-    f32x4 v = reinterpret_cast<const f32x4*>(cw)[c4] * t[1];
+    f32x4 v = reinterpret_cast<const f32x4*>(cw)[c4] * tot[1][g];
 #pragma unroll
     for (int i = 0; i < kTaps; ++i) {
-      reinterpret_cast<f32x4*>(dcw)[i * ncol4 + c4] = w * t[1 + i];
-      if (i > 0) v += reinterpret_cast<const f32x4*>(cw)[i * ncol4 + c4] * t[1 + i];
+      reinterpret_cast<f32x4*>(dcw)[i * ncol4 + c4] = w * tot[1 + i][g];
+      if (i > 0) v += reinterpret_cast<const f32x4*>(cw)[i * ncol4 + c4] * tot[1 + i][g];
     }
     reinterpret_cast<f32x4*>(dwv)[c4] = v;
   }
