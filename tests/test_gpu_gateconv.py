@@ -267,3 +267,41 @@ def test_gateconv_graph_capture_replays_match_eager(gpu):
         for x, t in outs.items():
             assert torch.equal(ref[x].view(torch.uint8), t.view(torch.uint8)), f"replay {r}: {x} differs"
         torch.ones(1 << 20, device=gpu).cumsum(0)  # unrelated eager work between replays
+
+
+def test_gateconv_max_rows(gpu):
+    """The largest accepted call, M*T = 4,194,304 rows (M = 1024 sequences of
+    T = 4096, d = 512): 512-row chunks, 8192 workgroups, 8192 partial blocks in
+    the reduce.  Every sequence holds the same data, so every sequence's
+    outputs must equal the first one's bit for bit (all sequences split into
+    chunks the same way), the first one's must match the oracle, and each
+    weight gradient must be M times the oracle's for one sequence."""
+    import torch
+    import memory_bound_engram_amd as eg
+    from gpu_util import u16
+    M, T, d = 1024, 4096, 512
+    assert M * T == eg.GATECONV_ROWS_MAX
+    one = synth.gateconv_inputs(1, T, d, seed=99)
+    big = {x: dev(one[x], gpu).expand(M, T, d).contiguous() for x in ("H", "k", "v", "dY")}
+    wh, wv, cw = dev(one["wh"], gpu), dev(one["wv"], gpu), dev(one["cw"], gpu)
+    Y, vhat = empty_bf16((M, T, d), gpu), empty_bf16((M, T, d), gpu)
+    al, rh, rk, rv = (empty_f32((M, T), gpu) for _ in range(4))
+    eg.engram_gateconv_fwd(big["H"], big["k"], big["v"], wh, wv, cw, Y, vhat, al, rh, rk, rv, eps=EPS)
+    dH, dk, dv = (empty_bf16((M, T, d), gpu) for _ in range(3))
+    dwh, dwv, dcw = empty_f32((d,), gpu), empty_f32((d,), gpu), empty_f32((4, d), gpu)
+    ws = torch.empty(eg.engram_gateconv_bwd_workspace_bytes(M, T, d), dtype=torch.uint8, device=gpu)
+    eg.engram_gateconv_bwd(big["dY"], big["H"], big["k"], big["v"], wh, wv, cw, vhat, al, rh, rk, rv,
+                           dH, dk, dv, dwh, dwv, dcw, ws)
+    torch.cuda.synchronize()
+    for t in (Y, vhat, al, rh, rk, rv, dH, dk, dv):
+        assert torch.equal(t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32),
+                           (t[:1].view(torch.int16) if t.dtype == torch.bfloat16 else t[:1].view(torch.int32))
+                           .expand_as(t)), "sequences differ"
+    got_f = {"Y": u16(Y[:1]), "vhat": u16(vhat[:1]), "alpha": al[:1].cpu().numpy(), "rh": rh[:1].cpu().numpy(),
+             "rk": rk[:1].cpu().numpy(), "rv": rv[:1].cpu().numpy()}
+    check_fwd(one, got_f, oracle_fwd(one))
+    saved = {"vhat": got_f["vhat"], "alpha": got_f["alpha"], "rh": got_f["rh"], "rk": got_f["rk"], "rv": got_f["rv"]}
+    ref = oracle_bwd(one, saved)
+    got_b = {"dH": u16(dH[:1]), "dk": u16(dk[:1]), "dv": u16(dv[:1]), "dwh": dwh.cpu().numpy() / M,
+             "dwv": dwv.cpu().numpy() / M, "dcw": dcw.cpu().numpy() / M}
+    check_bwd(got_b, ref)
