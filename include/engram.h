@@ -164,21 +164,25 @@ size_t engram_gate_bwd_workspace_bytes(int64_t N);
  * Shapes: H, k, v, Y, vhat, dY, dH, dk, dv [M][T][d] bf16; rms_w_h, rms_w_v
  * [d] fp32; conv_w [4][d] fp32; alpha, rrms_* [M][T] fp32; the weight
  * gradients are fp32 and overwritten.  d is a multiple of 512, at most 5120;
- * M, T >= 1 and M * T <= ENGRAM_GATECONV_ROWS_MAX.  All pointers device, 16-byte aligned, outputs overlapping
- * nothing; asynchronous on `stream`, no allocation or synchronisation.
+ * M, T >= 1 and M * T <= ENGRAM_GATECONV_ROWS_MAX.  All pointers device,
+ * 16-byte aligned, outputs overlapping nothing; asynchronous on `stream`, no
+ * allocation or synchronisation.  Errors as for the gate: ENGRAM_ERR_NULL,
+ * ENGRAM_ERR_N_RANGE (sizes, or eps outside [0, 1] or NaN), ENGRAM_ERR_ALIGN,
+ * ENGRAM_ERR_OVERLAP, all before any work is enqueued.
  * ========================================================================== */
 #define ENGRAM_GATECONV_D_MAX 5120
 #define ENGRAM_GATECONV_ROWS_MAX 4194304 /* M * T */
 
 /* Forward; argument order of the page's forward(H, k, v, rms_w_h, rms_w_v,
- * conv_w), then its returned list [Y, vhat, alpha, rrms_h, rrms_k, rrms_v]. */
+ * conv_w), then its returned list [Y, vhat, alpha, rrms_h, rrms_k, rrms_v],
+ * then the norms' eps (the page's default is 1e-6). */
 engram_status engram_gateconv_fwd(const void *H, const void *k, const void *v, const float *rms_w_h,
                                   const float *rms_w_v, const float *conv_w, void *Y, void *vhat, float *alpha,
                                   float *rrms_h, float *rrms_k, float *rrms_v, int64_t M, int64_t T, int64_t d,
                                   float eps, void *stream);
 
-/* Backward; argument order of the page's backward forward(dY, H, k, v,
- * rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k, rrms_v), then its
+/* Backward; argument order of the page's backward operator, forward(dY, H, k,
+ * v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k, rrms_v), then its
  * returned list [dH, dk, dv, drms_w_h, drms_w_v, dconv_w], then scratch of
  * engram_gateconv_bwd_workspace_bytes(M, T, d) bytes (contents ignored). */
 engram_status engram_gateconv_bwd(const void *dY, const void *H, const void *k, const void *v,
@@ -189,7 +193,7 @@ engram_status engram_gateconv_bwd(const void *dY, const void *H, const void *k, 
                                   int64_t d, void *stream);
 
 /* Scratch bytes of engram_gateconv_bwd (fp32 weight-gradient partials of each
- * token chunk); 0 for sizes the call would reject. */
+ * token chunk, then one fp32 per row); 0 for sizes the call would reject. */
 size_t engram_gateconv_bwd_workspace_bytes(int64_t M, int64_t T, int64_t d);
 
 /* Human-readable name of a status code (static storage). */
