@@ -33,7 +33,12 @@
 // every element is written once and the extra grad_out reads stay balanced.
 // The weight row of stream s sits in LDS.  Each wave accumulates a x k for its
 // vectors over its 64 / S tokens in VGPRs; the token slots are added in slot
-// order at the end.
+// order at the end.  The saved row of the slot's next token is fetched a token
+// ahead through the scalar cache.  Where delta is 0 -- a masked token (gate 0)
+// or the clamp path -- grad_x = G, grad_key = 0 and there is no grad_weight
+// term, so X, the key and the value are not read; for a masked token
+// grad_value is 0 too and the other streams' G are not read either.  (With
+// mask Bernoulli(0.3) that removes ~30% of the bytes.)
 // Kernel 2 (reduce): grad_weight[s][j] = sum over rows of the partials, in a
 // fixed order (32 contiguous row chunks summed sequentially, then the chunk
 // sums added in chunk order), so the result is bitwise reproducible.  When
@@ -85,10 +90,39 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
     for (int e = 0; e < kVec; ++e) acc[v][e] = 0.f;
   __syncthreads();
 
+  // the saved row (gate, dot, rstd_X, rstd_key of each stream; 64 bytes) of
+  // this slot's next token, fetched one token ahead through the scalar cache
+  // (the token index is wave-uniform), so no wait on it stalls the vector loads
+  auto token = [&](int jj) { return __builtin_amdgcn_readfirstlane((int)b + (u + kBwdSlots * jj) * nb); };
+  const f32x4* saved4 = reinterpret_cast<const f32x4*>(saved);
+  f32x4 svn[kStreams];
+  {
+    const int t0 = token(0);
+#pragma unroll
+    for (int so = 0; so < kStreams; ++so) svn[so] = saved4[t0 * kStreams + so];
+  }
+
   int buf = 0;
   for (int jj = 0; jj < kTokensPerSlot; ++jj) {
     const int k = u + kBwdSlots * jj;          // index of the token within row b
-    const int64_t t = b + (int64_t)k * nb;
+    const int64_t t = token(jj);
+    f32x4 sv[kStreams];
+#pragma unroll
+    for (int so = 0; so < kStreams; ++so) sv[so] = svn[so];
+    {
+      const int tn = token(jj + 1 < kTokensPerSlot ? jj + 1 : jj);
+#pragma unroll
+      for (int so = 0; so < kStreams; ++so) svn[so] = saved4[tn * kStreams + so];
+    }
+    const f32x4 own = s == 0 ? sv[0] : s == 1 ? sv[1] : s == 2 ? sv[2] : sv[3];
+    const float g = own[0], dot = own[1];
+    const float rx = own[2], rk = own[3];
+    // delta is 0 for a masked token (gate 0) and on the clamp path: then
+    // grad_x = G, grad_key = 0 and no grad_weight term, so X, the key and the
+    // value (needed only for dg) are not read.  A masked token's grad_value is
+    // 0 as well (every stream's gate is 0): the other streams' G are not read.
+    const bool live = g != 0.0f && fabsf(dot) >= kClamp;
+    const bool dv_zero = sv[0][0] == 0.0f && sv[1][0] == 0.0f && sv[2][0] == 0.0f && sv[3][0] == 0.0f;
     const uint16_t* gt = gout + t * (kStreams * kHidden);
     const uint16_t* xs = x + t * (kStreams * kHidden) + s * kHidden;
     const uint16_t* kt = kv + t * kKvCols;
@@ -96,40 +130,44 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
 
     u32x4 gr[kBwdVecs], vr[kBwdVecs], xr[kBwdVecs], kr[kBwdVecs], go[2][kStreams];
 #pragma unroll
-    for (int v = 0; v < kBwdVecs; ++v) {
-      const int col = (lane + 64 * (h + 2 * v)) * kVec;
-      gr[v] = load16(gt + s * kHidden + col);
-      vr[v] = load16(kt + kValueCol + col);
-      xr[v] = load16_stream(xs + col);
-      kr[v] = load16_stream(kt + s * kHidden + col);
+    for (int v = 0; v < kBwdVecs; ++v) gr[v] = load16(gt + s * kHidden + (lane + 64 * (h + 2 * v)) * kVec);
+    if (live) {
+#pragma unroll
+      for (int v = 0; v < kBwdVecs; ++v) {
+        const int col = (lane + 64 * (h + 2 * v)) * kVec;
+        vr[v] = load16(kt + kValueCol + col);
+        xr[v] = load16_stream(xs + col);
+        kr[v] = load16_stream(kt + s * kHidden + col);
+      }
     }
     // the other streams' grad_out at this wave's grad_value vectors
+    if (!dv_zero) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m == 1 && !dv_tail) continue;
-      const int col = (lane + 64 * (h + 2 * (m == 0 ? s : 4))) * kVec;
+      for (int m = 0; m < 2; ++m) {
+        if (m == 1 && !dv_tail) continue;
+        const int col = (lane + 64 * (h + 2 * (m == 0 ? s : 4))) * kVec;
 #pragma unroll
-      for (int so = 0; so < kStreams; ++so)
-        if (so != s) go[m][so] = load16(gt + so * kHidden + col);
+        for (int so = 0; so < kStreams; ++so)
+          if (so != s) go[m][so] = load16(gt + so * kHidden + col);
+      }
     }
 
     float p = 0.f;
+    if (live) {
 #pragma unroll
-    for (int v = 0; v < kBwdVecs; ++v)
+      for (int v = 0; v < kBwdVecs; ++v)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        p = fmaf(bf_lo(gr[v][q]), bf_lo(vr[v][q]), p);
-        p = fmaf(bf_hi(gr[v][q]), bf_hi(vr[v][q]), p);
-      }
+        for (int q = 0; q < 4; ++q) {
+          p = fmaf(bf_lo(gr[v][q]), bf_lo(vr[v][q]), p);
+          p = fmaf(bf_hi(gr[v][q]), bf_hi(vr[v][q]), p);
+        }
+    }
     p = wave_sum_to_lane63(p);
     if (lane == 63) red[buf][u][h] = p;
     __syncthreads();
     const float dg = red[buf][u][0] + red[buf][u][1];
     buf ^= 1;  // the next pair writes the other buffer: one barrier per pair suffices
 
-    const float* sv = saved + t * (kStreams * 4);
-    const float g = sv[4 * s + 0], dot = sv[4 * s + 1];
-    const float rx = sv[4 * s + 2], rk = sv[4 * s + 3];
     const float dz = dg * g * (1.0f - g);
     const float ad = fabsf(dot);
     const float delta = ad >= kClamp ? dz / (2.0f * sqrtf(ad)) : 0.0f;
@@ -140,40 +178,54 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
 
     uint16_t* dxs = dx + t * (kStreams * kHidden) + s * kHidden;
     uint16_t* dkt = dkv + t * kKvCols;
+    if (!live) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int v = 0; v < kBwdVecs; ++v) {
-      const int vec = lane + 64 * (h + 2 * v);
-      const f32x4 w0 = wrow[0][vec], w1 = wrow[1][vec];
-      const float wv[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-      u32x4 ox, ok;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float rdx[2], rdk[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int e = 2 * q + hh;
-          const float gx = hh ? bf_hi(gr[v][q]) : bf_lo(gr[v][q]);
-          const float xx = hh ? bf_hi(xr[v][q]) : bf_lo(xr[v][q]);
-          const float kk = hh ? bf_hi(kr[v][q]) : bf_lo(kr[v][q]);
-          rdx[hh] = fmaf(-cb, xx, fmaf(ca, wv[e] * kk, gx));
-          rdk[hh] = fmaf(-ce, kk, ca * (wv[e] * xx));
-          acc[v][e] = fmaf(ca, xx * kk, acc[v][e]);
-        }
-        ox[q] = pack_bf16x2(rdx[0], rdx[1]);
-        ok[q] = pack_bf16x2(rdk[0], rdk[1]);
+      for (int v = 0; v < kBwdVecs; ++v) {
+        const int vec = lane + 64 * (h + 2 * v);
+        store16_stream(dxs + vec * kVec, gr[v]);
+        store16_stream(dkt + s * kHidden + vec * kVec, zero);
       }
-      store16_stream(dxs + vec * kVec, ox);
-      store16_stream(dkt + s * kHidden + vec * kVec, ok);
+    } else {
+#pragma unroll
+      for (int v = 0; v < kBwdVecs; ++v) {
+        const int vec = lane + 64 * (h + 2 * v);
+        const f32x4 w0 = wrow[0][vec], w1 = wrow[1][vec];
+        const float wv[kVec] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        u32x4 ox, ok;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float rdx[2], rdk[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int e = 2 * q + hh;
+            const float gx = hh ? bf_hi(gr[v][q]) : bf_lo(gr[v][q]);
+            const float xx = hh ? bf_hi(xr[v][q]) : bf_lo(xr[v][q]);
+            const float kk = hh ? bf_hi(kr[v][q]) : bf_lo(kr[v][q]);
+            rdx[hh] = fmaf(-cb, xx, fmaf(ca, wv[e] * kk, gx));
+            rdk[hh] = fmaf(-ce, kk, ca * (wv[e] * xx));
+            acc[v][e] = fmaf(ca, xx * kk, acc[v][e]);
+          }
+          ox[q] = pack_bf16x2(rdx[0], rdx[1]);
+          ok[q] = pack_bf16x2(rdk[0], rdk[1]);
+        }
+        store16_stream(dxs + vec * kVec, ox);
+        store16_stream(dkt + s * kHidden + vec * kVec, ok);
+      }
     }
 
     // grad_value = sum over streams (order 0..3) of gate_s G_s, one bf16 cast
     float gh[kStreams];
 #pragma unroll
-    for (int so = 0; so < kStreams; ++so) gh[so] = sv[4 * so];
+    for (int so = 0; so < kStreams; ++so) gh[so] = sv[so][0];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       if (m == 1 && !dv_tail) continue;
       const int vec = lane + 64 * (h + 2 * (m == 0 ? s : 4));
+      if (dv_zero) {
+        store16_stream(dkt + kValueCol + vec * kVec, u32x4{0u, 0u, 0u, 0u});
+        continue;
+      }
       u32x4 ov;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
