@@ -78,6 +78,25 @@ def test_bwd_n8192_edge_rows(gpu):
         assert np.all(bf16_to_f64(dkv[t, s * 5120:(s + 1) * 5120]) == 0.0)
 
 
+def test_bwd_all_masked(gpu):
+    """Every token masked: the backward reads only grad_out and saved, and
+    writes grad_x = grad_out bit for bit, grad_kv = +0 and grad_weight = 0."""
+    import torch
+    from gpu_util import dev_inputs, f32, run_bwd, run_fwd, u16
+    n = 256
+    inp = synth.host_inputs(n, seed=3, p=0.0, grad=True)
+    assert not inp["mask"].any()
+    d = dev_inputs(inp, gpu)
+    out, saved = run_fwd(d)
+    gx, gkv, gw = run_bwd(d, saved)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out), inp["x"])
+    assert np.all(f32(saved)[:, :, 0] == 0.0)
+    assert np.array_equal(u16(gx), inp["grad_out"])
+    assert not u16(gkv).any()
+    assert not f32(gw).any()
+
+
 def test_fwd_bwd_repeated_1000_bitwise(gpu):
     """N = 8192 with the edge-row recipe, mask 0.3: 1000 forward+backward
     launches back to back on one stream; the last results equal the first
