@@ -411,6 +411,9 @@ def main():
                 "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(fwd_gbps / PEAK_GBPS, 4),
                 "launch_us": round(fwd_ms * 1e3, 2), "algorithmic_bytes_per_launch": fwd_bytes(n),
                 "traffic": recorded_traffic("fwd")}
+    # the HBM bytes the launch actually moves (masked tokens skip reads), over the same time
+    if roof["traffic"]:
+        roof["traffic_gbps"] = round(roof["traffic"] / (roof["launch_us"] * 1e-6) / 1e9, 1)
 
     res = {
         "metric": METRIC,
