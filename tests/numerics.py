@@ -1,6 +1,9 @@
 """Storage-type helpers and comparison rules shared by the tests.
 
-Comparison rules (each derived in the design notes from the arithmetic):
+Comparison rules (each derived from the fp32 arithmetic of the kernels: a
+value computed in fp32 differs from its exact value by at most a small
+multiple of the fp32 unit roundoff times the sum of the magnitudes of the
+terms that formed it, and the bf16 store adds one rounding):
 
 * bf16 outputs: the device value must lie within one bf16 ulp of the oracle's
   unrounded fp64 value, widened by an fp32-evaluation allowance

@@ -1,6 +1,7 @@
 """Element-by-element comparison of device results with the fp64 oracle.
 
-Bars (derivations in the design notes):
+Bars (from the fp32 evaluation error of each quantity, bounded by a multiple
+of the unit roundoff times the magnitude of its terms, plus the bf16 store):
   forward  rstd_X, rstd_key  rel 1e-5
            dot               1e-5 |dot| + 2^-22 A,  A = sum_j |x^ w k^|
            gate              1e-5 g + |dg/ddot| tol_dot;  exactly 0 when masked
