@@ -130,9 +130,22 @@ def cpu_baseline(seconds=10.0, sample=2048):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"fwd+bwd on the first {sample} tokens of the N={N_STEP} workload, "
-                      f"repeated {done // sample}x over {el:.1f} s (fp64, {threads} threads)"}
+    res = {"value": done / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"fwd+bwd on the first {sample} tokens of the N={N_STEP} workload, "
+                     f"repeated {done // sample}x over {el:.1f} s (fp64, {threads} threads)"}
+    # the same on one thread, over a smaller sample
+    one = inp["x"][:256], inp["kv"][:256], inp["mask"][:256], inp["grad_out"][:256]
+    done1, t1 = 0, time.perf_counter()
+    while True:
+        _, sv1 = oracle.fwd_bf16(one[0], one[1], inp["weight"], one[2], threads=1)
+        oracle.bwd_bf16(one[0], one[1], inp["weight"], sv1, one[3], threads=1)
+        done1 += 256
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 4:
+            break
+    res["single_thread"] = {"value": done1 / el1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"fwd+bwd on the first 256 tokens, repeated {done1 // 256}x over {el1:.1f} s"}
+    return res
 
 
 def bench_gateconv(torch, synth, eg, dev, stream, steps, R):
