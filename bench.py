@@ -112,6 +112,20 @@ def make_inputs(torch, synth, n, dev, grad):
     return x, kv, w, m, g
 
 
+def host_cpu():
+    """The host CPU's model name and logical CPU count (for the oracle baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(seconds=10.0, sample=2048):
     """The fp64 oracle on the host cores: fwd+bwd over the first `sample`
     tokens of the same workload, repeated until `seconds` have elapsed."""
@@ -145,6 +159,7 @@ def cpu_baseline(seconds=10.0, sample=2048):
             break
     res["single_thread"] = {"value": done1 / el1, "unit": "tokens/s", "cores": 1,
                             "sample": f"fwd+bwd on the first 256 tokens, repeated {done1 // 256}x over {el1:.1f} s"}
+    res["host"] = host_cpu()
     return res
 
 
@@ -325,6 +340,8 @@ def bench_configs(torch, synth, eg, dev, stream, with_cpu, rotate):
         torch.cuda.empty_cache()
         if with_cpu:
             line["oracle"] = oracle_rate(op, n, c["mask_p"], c["edge"])
+            line["oracle"]["host"] = host_cpu()
+            line["speedup_vs_oracle"] = round(line["tokens_per_s"] / line["oracle"]["tokens_per_s"], 1)
         print(json.dumps(line), flush=True)
 
 
