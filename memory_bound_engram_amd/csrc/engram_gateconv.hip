@@ -25,7 +25,8 @@
 // intermediates.  Each thread covers C columns of a row (the column map
 // below): d = 5120 runs 512 threads x 10 columns (an octet and a pair), so
 // the workgroup is a power of two and each thread has 256 VGPRs; other widths
-// run d/8 threads x 8 columns (one octet).  Row sums reduce with DPP inside
+// run d/8 threads x 8 columns (one octet), except the backward at d = 512 and
+// 1024, which runs d/2 threads x 2 columns (one pair).  Row sums reduce with DPP inside
 // each wave and across waves through LDS, in a fixed order.  Weight gradients
 // are per-workgroup fp32 partials in the workspace, summed by a last kernel
 // in a fixed order.
@@ -762,23 +763,30 @@ gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restric
 }
 
 // The column map for width d = 512 nw: 512 threads x 10 columns for d = 5120,
-// else 64 nw threads x 8 columns.
+// else 64 nw threads x 8 columns.  The backward of the two narrowest widths
+// runs 256 nw threads x 2 columns instead: four times the waves for rows of
+// only 1-2 KB, where one wave per 512 columns leaves the CUs with too few
+// waves to hide the latency of each row step (14% faster at d = 512 and 1024;
+// the forward gains nothing from it).
 template <int NW>
 using MapFor = std::conditional_t<NW == 10, ColMap<512, 10>, ColMap<64 * NW, 8>>;
+template <int NW>
+using BwdMapFor = std::conditional_t<NW <= 2, ColMap<256 * NW, 2>, MapFor<NW>>;
 
 struct Kernels {
   const void* fwd;
   const void* conv;
   const void* hk;
-  int threads;
+  int fwd_threads, bwd_threads;
 };
 
 template <int NW>
 Kernels kernels_for() {
   using MP = MapFor<NW>;
+  using MB = BwdMapFor<NW>;
   return {reinterpret_cast<const void*>(&gateconv_fwd_kernel<MP>),
-          reinterpret_cast<const void*>(&gateconv_bwd_conv_kernel<MP>),
-          reinterpret_cast<const void*>(&gateconv_bwd_hk_kernel<MP>), MP::THREADS};
+          reinterpret_cast<const void*>(&gateconv_bwd_conv_kernel<MB>),
+          reinterpret_cast<const void*>(&gateconv_bwd_hk_kernel<MB>), MP::THREADS, MB::THREADS};
 }
 
 const Kernels* kernels_for_width(int64_t d) {
@@ -822,7 +830,7 @@ hipError_t launch_gateconv_fwd(const void* H, const void* K, const void* V, cons
   uint16_t *yp = static_cast<uint16_t*>(Y), *vhp = static_cast<uint16_t*>(vhat);
   int rows = (int)(M * T), Ti = (int)T, ch = chunk;
   void* args[] = {&hp, &kp, &vp, &wh, &wv, &cw, &yp, &vhp, &alpha, &rrh, &rrk, &rrv, &rows, &Ti, &ch, &eps};
-  return hipLaunchKernel(kn->fwd, dim3((unsigned)gateconv_workgroups(M, T, chunk)), dim3((unsigned)kn->threads), args,
+  return hipLaunchKernel(kn->fwd, dim3((unsigned)gateconv_workgroups(M, T, chunk)), dim3((unsigned)kn->fwd_threads), args,
                          0, stream);
 }
 
@@ -842,11 +850,11 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
   float* ds = partial + nwg * kPartRows * d;
   int rows = (int)(M * T), Ti = (int)T, di = (int)d, ch = chunk;
   void* a1[] = {&gp, &vp, &wv, &cw, &vhp, &alpha, &rrv, &dvp, &ds, &partial, &rows, &Ti, &ch};
-  hipError_t e = hipLaunchKernel(kn->conv, dim3((unsigned)nwg), dim3((unsigned)kn->threads), a1, 0, stream);
+  hipError_t e = hipLaunchKernel(kn->conv, dim3((unsigned)nwg), dim3((unsigned)kn->bwd_threads), a1, 0, stream);
   if (e != hipSuccess) return e;
   const float* dsc = ds;
   void* a2[] = {&hp, &kp, &wh, &dsc, &rrh, &rrk, &dhp, &dkp, &partial, &rows};
-  e = hipLaunchKernel(kn->hk, dim3((unsigned)nwg), dim3((unsigned)kn->threads), a2, 0, stream);
+  e = hipLaunchKernel(kn->hk, dim3((unsigned)nwg), dim3((unsigned)kn->bwd_threads), a2, 0, stream);
   if (e != hipSuccess) return e;
   const float* cp = partial;
   int nwi = (int)nwg;
