@@ -57,6 +57,41 @@ MUTANTS = [
     ("gateconv dwh drops the key path", "dwh[j] += dhh * Ht[j] * rh + dkh * kt[j] * rk;", "dwh[j] += dhh * Ht[j] * rh;"),
     ("gateconv dcw pairs the wrong token", "dcw[(int64_t)i * d + j] += dc[t * d + j] * u[tau * d + j];",
      "dcw[(int64_t)i * d + j] += dc[t * d + j] * u[t * d + j];"),
+    # tolerance scales (the magnitudes that set the parity bars)
+    ("dot conditioning x1000", "absdot += fabs(term);", "absdot += 1000.0 * fabs(term);"),
+    ("mag_dx x1000", "mdx[(int64_t)s * d + j] = fabs(Gs[j]) + dmag",
+     "mdx[(int64_t)s * d + j] = 1000.0 * fabs(Gs[j]) + 1000.0 * dmag"),
+    ("mag_dw x1000", "mdw[(int64_t)s * d + j] += dmag * fabs(xh * kh);",
+     "mdw[(int64_t)s * d + j] += 1000.0 * dmag * fabs(xh * kh);"),
+    ("mag_dx drops |G|", "mdx[(int64_t)s * d + j] = fabs(Gs[j]) + dmag", "mdx[(int64_t)s * d + j] = dmag"),
+    ("mag_dx drops the dot term", "(fabs(ws[j] * kh) + fabs(dot * xh) / (double)d)", "fabs(ws[j] * kh)"),
+    ("mag_dk drops the dot term", "dmag * rk * (fabs(ws[j] * xh) + fabs(dot * kh) / (double)d)",
+     "dmag * rk * fabs(ws[j] * xh)"),
+    ("mag_dv drops the gate", "if (mdv) mdv[j] += fabs(gate * Gs[j]);", "if (mdv) mdv[j] += fabs(Gs[j]);"),
+    ("delta magnitude from |dg| instead of sum |G v|", "dgabs * gate * (1.0 - gate) / (2.0 * sqrt(fabs(dot)))",
+     "fabs(dg) * gate * (1.0 - gate) / (2.0 * sqrt(fabs(dot)))"),
+    ("gate slope drops the 2", "if (fabs(dot) >= c) return g * (1.0 - g) / (2.0 * sqrt(fabs(dot)));",
+     "if (fabs(dot) >= c) return g * (1.0 - g) / sqrt(fabs(dot));"),
+    ("gate slope kept for masked tokens", "aux[2 * s + 1] = m ? gate_slope(dot, g) : 0.0;",
+     "aux[2 * s + 1] = gate_slope(dot, g);"),
+    ("gateconv magY drops the residual", "fabs(silu_grad(c)) * cm + fabs(vhat[t * d + j]) +",
+     "fabs(silu_grad(c)) * cm +"),
+    ("gateconv m(u) ignores alpha", "um_scr[t * d + j] = fabs(u_scr[t * d + j]) * (1.0 + (a > 0.0 ? 2.0 * da_scr[t] / a : 0.0));",
+     "um_scr[t * d + j] = fabs(u_scr[t * d + j]);"),
+    ("gateconv m(alpha) drops the logit magnitude", "da_scr[t] = a * (1.0 - a) * smag;", "da_scr[t] = a * (1.0 - a);"),
+    ("gateconv m(dc) drops the SiLU'' term", "dcm[t * d + j] = fabs(dY[t * d + j]) * (fabs(g) + 0.5 * cm);",
+     "dcm[t * d + j] = fabs(dY[t * d + j]) * fabs(g);"),
+    ("gateconv magH x1000", "if (magH) magH[t * d + j] = rh * (", "if (magH) magH[t * d + j] = 1000.0 * rh * ("),
+    ("gateconv mag_dconv_w x1000", "if (mdcw) mdcw[(int64_t)i * d + j] += dcm[t * d + j] * fabs(u[tau * d + j]);",
+     "if (mdcw) mdcw[(int64_t)i * d + j] += 1000.0 * dcm[t * d + j] * fabs(u[tau * d + j]);"),
+    ("gateconv mag_drms_w_v drops rrms_v", "if (mdwv) mdwv[j] += dum * fabs(vh[j] * rv);",
+     "if (mdwv) mdwv[j] += dum * fabs(vh[j]);"),
+    ("gateconv magv misses alpha", "if (magv) magv[t * d + j] *= a;", "if (magv) magv[t * d + j] *= 1.0;"),
+    ("gateconv mag_drms_w_h drops the key path",
+     "if (mdwh) mdwh[j] += dsm * (fabs(kh * Ht[j] * rh) + fabs(hh * kt[j] * rk)) / sd;",
+     "if (mdwh) mdwh[j] += dsm * fabs(kh * Ht[j] * rh) / sd;"),
+    ("gateconv row-sum magnitudes swapped", "const double s2m = dsm / sd * rk * pm, s3m = dsm / sd * rh * pm;",
+     "const double s2m = dsm / sd * rh * pm, s3m = dsm / sd * rk * pm;"),
 ]
 
 
@@ -72,6 +107,7 @@ def test_pins_reject_mutant(desc, old, new, tmp_path):
     env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_gateconv_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_gateconv_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_tolerance_scales.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
