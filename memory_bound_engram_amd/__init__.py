@@ -1,8 +1,9 @@
 """libengram: the four-stream Engram saved-state gate on AMD MI355X (gfx950).
 
 A thin ctypes binding over the C ABI declared in ``include/engram.h``.  It only
-marshals arguments (device pointers, N, the current stream); every step of
-the computation runs in the HIP kernels of ``libengram.so``.  There is no
+marshals arguments (device pointers, N, the current stream) after checking
+that each tensor has the element type, size and device the call will touch;
+every step of the computation runs in the HIP kernels of ``libengram.so``.  There is no
 fallback: if the library is missing, importing this package raises.
 
 PyTorch is used only as a source of device memory and streams.
@@ -99,6 +100,69 @@ def _ptr(t):
     return t.data_ptr()
 
 
+# Host-side checks of tensor arguments against the sizes a call will touch.
+# The C ABI sees raw pointers only, so a tensor shorter than N rows, of the
+# wrong element type or on another device would become out-of-bounds device
+# accesses; these checks turn every such call into a ValueError before
+# anything reaches the library.  A raw integer address is passed through
+# unchecked: the caller then vouches for its size.
+_BF16, _F32 = "bfloat16", "float32"
+_BYTE_DTYPES = ("bool", "uint8", "int8")
+
+
+def _dtype_name(t):
+    return str(t.dtype).replace("torch.", "")
+
+
+def _check_tensors(specs):
+    """specs: (name, tensor or None or int, allowed dtype names, minimum element
+    count).  Every tensor must have one of its dtypes, hold at least that many
+    elements, be contiguous and live on the same CUDA/HIP device."""
+    specs = [sp for sp in specs if sp[1] is not None and not isinstance(sp[1], int)]
+    for name, t, dtypes, need in specs:
+        if _dtype_name(t) not in dtypes:
+            raise ValueError(f"{name}: dtype {_dtype_name(t)}, expected {' or '.join(dtypes)}")
+        if t.numel() < need:
+            raise ValueError(f"{name}: {t.numel()} elements, the call needs at least {need}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: libengram needs contiguous tensors")
+    device = None
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: on {t.device}, libengram needs GPU (HIP) tensors")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name}: on {t.device}, other arguments on {device}")
+
+
+def _check_n(N, lo, hi):
+    if not isinstance(N, int) or isinstance(N, bool):
+        raise ValueError(f"N must be an int, got {type(N).__name__}")
+    # sizes outside the accepted range are left to the library, which
+    # rejects them with its own status (nothing would be touched)
+    return lo <= N <= hi
+
+
+def _gate_specs(N, x=None, kv=None, weight=None, mask=None, saved=None, grad_out=None, grad_x=None,
+                grad_kv=None, grad_weight=None, workspace=None, out=None):
+    row, kvrow = STREAMS * HIDDEN, KV_COLS
+    return [("x", x, (_BF16,), N * row), ("kv", kv, (_BF16,), N * kvrow),
+            ("weight", weight, (_F32,), STREAMS * HIDDEN), ("mask", mask, _BYTE_DTYPES, N),
+            ("out", out, (_BF16,), N * row), ("saved", saved, (_F32,), N * STREAMS * 4),
+            ("grad_out", grad_out, (_BF16,), N * row), ("grad_x", grad_x, (_BF16,), N * row),
+            ("grad_kv", grad_kv, (_BF16,), N * kvrow), ("grad_weight", grad_weight, (_F32,), STREAMS * HIDDEN),
+            ("workspace", workspace, _BYTE_DTYPES + (_F32,), 0)]
+
+
+def _check_workspace(workspace, need_bytes):
+    if workspace is None or isinstance(workspace, int):
+        return
+    have = workspace.numel() * workspace.element_size()
+    if have < need_bytes:
+        raise ValueError(f"workspace: {have} bytes, the call needs {need_bytes}")
+
+
 def _stream(stream, *tensors):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -123,6 +187,8 @@ def engram_gate_fwd(x, kv, weight, mask, out, saved, N=None, stream=None) -> Non
     """
     if N is None:
         N = x.shape[0]
+    if _check_n(N, 1, N_MAX):
+        _check_tensors(_gate_specs(N, x=x, kv=kv, weight=weight, mask=mask, out=out, saved=saved))
     _check(lib.engram_gate_fwd(_ptr(x), _ptr(kv), _ptr(weight), _ptr(mask), _ptr(out), _ptr(saved), N,
                                _stream(stream, x)))
 
@@ -137,8 +203,16 @@ def engram_gate_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight
     """
     if N is None:
         N = x.shape[0]
+    _check_bwd_args(N, x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace)
     _check(lib.engram_gate_bwd(_ptr(x), _ptr(kv), _ptr(weight), _ptr(saved), _ptr(grad_out), _ptr(grad_x),
                                _ptr(grad_kv), _ptr(grad_weight), _ptr(workspace), N, _stream(stream, x)))
+
+
+def _check_bwd_args(N, x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace, extra=()):
+    if _check_n(N, 1, BWD_N_MAX):
+        _check_workspace(workspace, engram_gate_bwd_workspace_bytes(N))
+        _check_tensors(_gate_specs(N, x=x, kv=kv, weight=weight, saved=saved, grad_out=grad_out, grad_x=grad_x,
+                                   grad_kv=grad_kv, grad_weight=grad_weight, workspace=workspace) + list(extra))
 
 
 def engram_gate_bwd_with_norm_weights(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we,
@@ -147,6 +221,10 @@ def engram_gate_bwd_with_norm_weights(x, kv, weight, saved, grad_out, grad_x, gr
     for weight = wh * we (wh, we [4,5120] bf16; grad_wh, grad_we [4,5120] fp32)."""
     if N is None:
         N = x.shape[0]
+    w = STREAMS * HIDDEN
+    _check_bwd_args(N, x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, workspace,
+                    [("wh", wh, (_BF16,), w), ("we", we, (_BF16,), w), ("grad_wh", grad_wh, (_F32,), w),
+                     ("grad_we", grad_we, (_F32,), w)])
     _check(lib.engram_gate_bwd_with_norm_weights(
         _ptr(x), _ptr(kv), _ptr(weight), _ptr(saved), _ptr(grad_out), _ptr(grad_x), _ptr(grad_kv),
         _ptr(grad_weight), _ptr(wh), _ptr(we), _ptr(grad_wh), _ptr(grad_we), _ptr(workspace), N,
@@ -155,6 +233,8 @@ def engram_gate_bwd_with_norm_weights(x, kv, weight, saved, grad_out, grad_x, gr
 
 def engram_fused_weight(wh, we, weight, stream=None) -> None:
     """weight [4,5120] fp32 = float(wh) * float(we), wh and we [4,5120] bf16 (exact)."""
+    w = STREAMS * HIDDEN
+    _check_tensors([("wh", wh, (_BF16,), w), ("we", we, (_BF16,), w), ("weight", weight, (_F32,), w)])
     _check(lib.engram_fused_weight(_ptr(wh), _ptr(we), _ptr(weight), _stream(stream, wh)))
 
 
@@ -172,6 +252,12 @@ def engram_gateconv_fwd(H, k, v, rms_w_h, rms_w_v, conv_w, Y, vhat, alpha, rrms_
     """Enqueue the GateConv forward.  H, k, v, Y, vhat [M,T,d] bf16; rms_w_h,
     rms_w_v [d] fp32; conv_w [4,d] fp32; alpha, rrms_* [M,T] fp32 (written)."""
     M, T, d = H.shape
+    rows = M * T
+    _check_tensors([(n_, t_, (_BF16,), rows * d) for n_, t_ in (("H", H), ("k", k), ("v", v), ("Y", Y), ("vhat", vhat))]
+                   + [(n_, t_, (_F32,), rows) for n_, t_ in (("alpha", alpha), ("rrms_h", rrms_h), ("rrms_k", rrms_k),
+                                                             ("rrms_v", rrms_v))]
+                   + [("rms_w_h", rms_w_h, (_F32,), d), ("rms_w_v", rms_w_v, (_F32,), d),
+                      ("conv_w", conv_w, (_F32,), 4 * d)])
     _check(lib.engram_gateconv_fwd(_ptr(H), _ptr(k), _ptr(v), _ptr(rms_w_h), _ptr(rms_w_v), _ptr(conv_w), _ptr(Y),
                                    _ptr(vhat), _ptr(alpha), _ptr(rrms_h), _ptr(rrms_k), _ptr(rrms_v), M, T, d, eps,
                                    _stream(stream, H)))
@@ -183,6 +269,17 @@ def engram_gateconv_bwd(dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms
     dv [M,T,d] bf16 and drms_w_h, drms_w_v [d], dconv_w [4,d] fp32 are written
     in full; workspace holds engram_gateconv_bwd_workspace_bytes(M, T, d) bytes."""
     M, T, d = H.shape
+    rows = M * T
+    _check_workspace(workspace, engram_gateconv_bwd_workspace_bytes(M, T, d))
+    _check_tensors([(n_, t_, (_BF16,), rows * d)
+                    for n_, t_ in (("dY", dY), ("H", H), ("k", k), ("v", v), ("vhat", vhat), ("dH", dH), ("dk", dk),
+                                   ("dv", dv))]
+                   + [(n_, t_, (_F32,), rows) for n_, t_ in (("alpha", alpha), ("rrms_h", rrms_h), ("rrms_k", rrms_k),
+                                                             ("rrms_v", rrms_v))]
+                   + [(n_, t_, (_F32,), d) for n_, t_ in (("rms_w_h", rms_w_h), ("rms_w_v", rms_w_v),
+                                                          ("drms_w_h", drms_w_h), ("drms_w_v", drms_w_v))]
+                   + [("conv_w", conv_w, (_F32,), 4 * d), ("dconv_w", dconv_w, (_F32,), 4 * d),
+                      ("workspace", workspace, _BYTE_DTYPES + (_F32,), 0)])
     _check(lib.engram_gateconv_bwd(_ptr(dY), _ptr(H), _ptr(k), _ptr(v), _ptr(rms_w_h), _ptr(rms_w_v), _ptr(conv_w),
                                    _ptr(vhat), _ptr(alpha), _ptr(rrms_h), _ptr(rrms_k), _ptr(rrms_v), _ptr(dH),
                                    _ptr(dk), _ptr(dv), _ptr(drms_w_h), _ptr(drms_w_v), _ptr(dconv_w),

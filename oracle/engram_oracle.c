@@ -9,17 +9,18 @@
  *
  * Sources (web pages; cited by title and paragraph):
  *   [GATE]  "Engram saved-state gate", cuDNN frontend documentation.
- *           - semantics paragraph: per token and stream, X and its key are
- *             RMS-normalised separately (eps 1e-20), x^ * weight * k^ is
- *             reduced in FP32, passed through a signed square root whose
- *             magnitude is clamped below at 1e-6, then a sigmoid; the output
- *             is X + gate * shared value, rounded once to BF16; a false token
- *             mask leaves X unchanged; weight is the FP32 product of the
- *             source q/k norm weights.
- *           - layout paragraph: packed KV holds four keys in its first
- *             4*5120 columns and the shared value in the last 5120; backward
- *             writes the same packed layout and sums the four shared-value
- *             contributions before the single BF16 cast.
+ *           - semantics paragraph: the map evaluated here, per token t and
+ *             stream s, with m the token's mask bit:
+ *               r_x = (mean_j x_j^2 + eps)^(-1/2),  r_k the same for the key
+ *               dot = sum_j (r_x x_j) w_j (r_k k_j)          (eps = 1e-20)
+ *               gate = sigmoid(sgn(dot) * sqrt(max(|dot|, 1e-6)))
+ *               out = m ? bf16(x + gate v) : x
+ *             where w is a weight the caller forms as a product of two
+ *             normalisation weights (fused_weight below).
+ *           - layout paragraph: a KV row is [key 0 | key 1 | key 2 | key 3 |
+ *             value], 5120 columns each; grad_kv uses the same packing, and
+ *             its value part is one bf16 rounding of the fp32 sum over the
+ *             four streams.
  *           - saved-state paragraph: saved holds (gate, dot, rstd_X,
  *             rstd_key) per stream.
  *   [TK]    "tile-kernels 1.0.0" sdist listing, tests/engram/

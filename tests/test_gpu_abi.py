@@ -16,7 +16,7 @@ def test_rejected_calls_do_not_touch_outputs(gpu):
     from gpu_util import alloc_bwd, dev_inputs, poison
     inp = synth.host_inputs(100, seed=1, p=0.9, grad=True)
     d = dev_inputs(inp, gpu)
-    gx, gkv, gw, ws = alloc_bwd(d["x"], d["kv"], 64)
+    gx, gkv, gw, ws = alloc_bwd(d["x"], d["kv"], 100)  # sized for N = 100: the library's own check fires
     saved = torch.zeros((100, 4, 4), dtype=torch.float32, device=gpu)
     with pytest.raises(eg.EngramError) as e:
         eg.engram_gate_bwd(d["x"], d["kv"], d["weight"], saved, d["grad_out"], gx, gkv, gw, ws, 100)

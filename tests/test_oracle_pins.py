@@ -57,7 +57,7 @@ def test_bf16_nan_stays_quiet_nan():
 
 
 # --------------------------------------------------------------------------
-# masking: a false mask leaves X unchanged (semantics paragraph)
+# masking: a masked token's output is its X row, bit for bit (semantics paragraph)
 # --------------------------------------------------------------------------
 
 def test_mask_false_output_is_x_bitwise_and_gradients_vanish():
