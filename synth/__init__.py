@@ -63,7 +63,9 @@ _dev = None
 def _h():
     global _host
     if _host is None:
-        lib = ctypes.CDLL(build_host())
+        # ENGRAM_SYNTH_HOST_LIB names another build of synth_host.c (the
+        # sanitizer test loads an instrumented one)
+        lib = ctypes.CDLL(os.environ.get("ENGRAM_SYNTH_HOST_LIB") or build_host())
         P, I64, U64, U32, I = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_uint32,
                                ctypes.c_int)
         lib.synth_stream_key.argtypes = [U64, U32]
