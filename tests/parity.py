@@ -13,7 +13,16 @@ of the unit roundoff times the magnitude of its terms, plus the bf16 store):
                              32 u32 (magnitude scale from the oracle, which bounds
                              delta through sum |G v|); norm-wise rel L2 against the
                              oracle's rounded bf16 values <= 2e-3
-           grad_weight       1e-3 |ref| + 2^-17 C,  C = sum_t |delta x^ k^|
+           grad_weight       1e-3 |ref| + 1e-4 + 2^-20 C,  C = sum_t |delta| x^ k^|
+                             with |delta| bounded through sum |G v| as above.
+                             The worst-case rounding bound of the device's
+                             summation (about 120 sequential fp32 roundings per
+                             element: the grad-of-gate reduction inside delta,
+                             32 tokens per wave, the slot combine, then the
+                             partial-row reduction) is ~2^-17 C; the bar uses
+                             the tighter 2^-20 C, which the rounding errors,
+                             being independent, stay far below (the largest
+                             |error| / C seen is reported as dw_err_over_C).
 """
 from __future__ import annotations
 
@@ -108,7 +117,11 @@ def check_bwd(inp, saved32, dx16, dkv16, dw32, threads=8, ref=None):
             sl = slice(c0, c0 + CHUNK)
             agg.add(check_bf16(name, got[sl], r64[sl], mag[sl]))
         agg.report(st, key)
-    st["dw_maxrel"] = check_rel("grad_weight", dw32, dw64, 1e-3, atol=2.0 ** -17 * mdw)
+    st["dw_maxrel"] = check_rel("grad_weight", dw32, dw64, 1e-3, atol=1e-4 + 2.0 ** -20 * mdw)
+    err = np.abs(dw32.astype(np.float64) - dw64)
+    st["dw_err_over_C"] = float(np.max(err / np.maximum(mdw, 1e-300)))
+    # elements outside a plain rel 1e-3 / abs 1e-4 bar (allowed by the C term where the sum cancels)
+    st["dw_outside_rel1e-3_abs1e-4"] = int(np.count_nonzero(err > 1e-3 * np.abs(dw64) + 1e-4))
     st["dw_rel_l2"] = _rel_l2(dw32, dw64)
     for k in ("dx_rel_l2", "dkv_rel_l2", "dw_rel_l2"):
         assert st[k] <= 2e-3, f"{k} = {st[k]:.3e} exceeds 2e-3"

@@ -123,3 +123,54 @@ def test_fwd_bwd_repeated_1000_bitwise(gpu):
     torch.cuda.synchronize()
     for a, b in zip(first[:5], again[:5]):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_config4_fwd_bwd_1000_launches_vs_oracle(gpu):
+    """The edge-row workload as a whole: N = 8192 (the backward maximum),
+    mask Bernoulli(0.3), 5% of rows with X or a key scaled by 1e-12 (eps
+    path), 10% with keys inside the clamp band, all-zero rows; 1000 forward +
+    backward launches back to back on one stream, then the last launch's
+    results against the oracle on the same input bytes:
+      - the device forward, every element (out, saved);
+      - the device backward on the device's own saved, elementwise, with the
+        oracle consuming that same saved;
+      - the device chain against the oracle chain (oracle forward, then
+        oracle backward), norm-wise;
+      - masked and clamp-path rows exactly (grad_x = grad_out bit for bit,
+        grad_key = 0)."""
+    import torch
+    import memory_bound_engram_amd as eg
+    from gpu_util import alloc_bwd, dev_inputs, f32, poison, u16
+    from numerics import bf16_to_f64
+    from parity import check_bwd, check_bwd_end_to_end, check_fwd
+    n = 8192
+    inp = synth.host_inputs(n, seed=0, p=0.3, grad=True, edge=True)
+    counts = inp["edge_counts"]
+    print("edge rows:", counts, flush=True)
+    d = dev_inputs(inp, gpu)
+    x, kv, w, m, g = d["x"], d["kv"], d["weight"], d["mask"], d["grad_out"]
+    out = poison(torch.empty_like(x))
+    saved = poison(torch.empty((n, 4, 4), dtype=torch.float32, device=gpu))
+    gx, gkv, gw, ws = alloc_bwd(x, kv, n)
+    for _ in range(1000):
+        eg.engram_gate_fwd(x, kv, w, m, out, saved, n)
+        eg.engram_gate_bwd(x, kv, w, saved, g, gx, gkv, gw, ws, n)
+    torch.cuda.synchronize()
+    out_h, saved_h = u16(out), f32(saved)
+    dx, dkv, dw = u16(gx), u16(gkv), f32(gw)
+    fwd_ref = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=16, extras=True)
+    st_f = check_fwd(inp, out_h, saved_h, ref=fwd_ref)
+    st_b = check_bwd(inp, saved_h, dx, dkv, dw, threads=16)
+    st_e = check_bwd_end_to_end(inp, saved_h, dx, dkv, dw, fwd_ref, threads=16)
+    print(st_f, st_b, st_e)
+    off = inp["mask"] == 0
+    assert np.array_equal(dx[off], inp["grad_out"][off])
+    assert np.all(bf16_to_f64(dkv[off]) == 0.0)
+    dots = saved_h[:, :, 1]
+    clamp = np.abs(dots) < np.float32(1e-6)
+    assert 0.08 < clamp.mean() < 0.12          # the workload puts 10% of the dots inside the clamp
+    t_idx, s_idx = np.nonzero(clamp & ~off[:, None])
+    assert t_idx.size > 100
+    for t, s in zip(t_idx, s_idx):
+        assert np.array_equal(dx[t, s], inp["grad_out"][t, s])
+        assert np.all(bf16_to_f64(dkv[t, s * 5120:(s + 1) * 5120]) == 0.0)
