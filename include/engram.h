@@ -40,9 +40,11 @@
  *     each other; outputs and workspace must not overlap any input or each
  *     other (saved-state paragraph).
  *   - The library holds no state between calls beyond per-device caches of
- *     fixed facts (the CU count), and is thread-safe; calls on different
- *     streams are independent.  Results are bitwise
- *     reproducible for identical inputs (fixed reduction orders, no atomics).
+ *     fixed facts (the CU count, the address of its own scratch array), and
+ *     is thread-safe; calls on different streams are independent, except
+ *     engram_gate_bwd_noalloc calls on one GPU, which share that GPU's
+ *     scratch array.  Results are bitwise reproducible for identical inputs
+ *     (fixed reduction orders, no atomics).
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H
@@ -133,6 +135,30 @@ engram_status engram_gate_bwd_with_norm_weights(const void *x, const void *kv, c
                                                 void *grad_kv, float *grad_weight, const void *wh,
                                                 const void *we, float *grad_wh, float *grad_we,
                                                 void *workspace, int64_t N, void *stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Same arguments, results and
+ * contract as engram_gate_bwd without `workspace`: the grad_weight partial
+ * rows go to a fixed array inside the library, sized for
+ * ENGRAM_NOALLOC_N_MAX tokens (ENGRAM_NOALLOC_SCRATCH_BYTES = 10 MiB), which
+ * every GPU the library runs on holds from its first such call until the
+ * process ends.  Results are bit-identical to engram_gate_bwd's.
+ *   N   64 <= N <= ENGRAM_NOALLOC_N_MAX (= the backward's own limit), N % 64 == 0;
+ *       larger N returns ENGRAM_ERR_N_RANGE before anything is enqueued.
+ * The first call on a device looks up the array's address on that device
+ * (the current device; a failure returns ENGRAM_ERR_LAUNCH).  No call
+ * allocates, frees or synchronises.  Every call on one GPU shares its array:
+ * nothing carries over from one call to the next, but calls that overlap in
+ * time on one GPU (on different streams) race and must be serialised by the
+ * caller.
+ */
+#define ENGRAM_NOALLOC_N_MAX 8192
+#define ENGRAM_NOALLOC_SCRATCH_BYTES 10485760 /* (8192/64) * 4 * 5120 * 4 */
+engram_status engram_gate_bwd_noalloc(const void *x, const void *kv, const float *weight, const float *saved,
+                                      const void *grad_out, void *grad_x, void *grad_kv, float *grad_weight,
+                                      int64_t N, void *stream);
 
 /*
  * Fused weight: weight = float(wh) * float(we), [4][5120] bf16 inputs, fp32

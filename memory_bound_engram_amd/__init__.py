@@ -59,6 +59,8 @@ lib.engram_gate_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
 lib.engram_gate_bwd.restype = ctypes.c_int
 lib.engram_gate_bwd_with_norm_weights.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
 lib.engram_gate_bwd_with_norm_weights.restype = ctypes.c_int
+lib.engram_gate_bwd_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _P]
+lib.engram_gate_bwd_noalloc.restype = ctypes.c_int
 lib.engram_fused_weight.argtypes = [_P, _P, _P, _P]
 lib.engram_fused_weight.restype = ctypes.c_int
 lib.engram_gate_bwd_workspace_bytes.argtypes = [_I64]
@@ -231,6 +233,23 @@ def engram_gate_bwd_with_norm_weights(x, kv, weight, saved, grad_out, grad_x, gr
         _stream(stream, x)))
 
 
+NOALLOC_N_MAX = 8192
+
+
+def engram_gate_bwd_noalloc(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, N=None,
+                            stream=None) -> None:
+    """engram_gate_bwd without a workspace, for callers that cannot allocate:
+    the partial rows live in the library's own per-GPU array (N <= 8192).
+    Calls that overlap in time on one GPU race on that array."""
+    if N is None:
+        N = x.shape[0]
+    if _check_n(N, 1, NOALLOC_N_MAX):
+        _check_tensors(_gate_specs(N, x=x, kv=kv, weight=weight, saved=saved, grad_out=grad_out, grad_x=grad_x,
+                                   grad_kv=grad_kv, grad_weight=grad_weight))
+    _check(lib.engram_gate_bwd_noalloc(_ptr(x), _ptr(kv), _ptr(weight), _ptr(saved), _ptr(grad_out), _ptr(grad_x),
+                                       _ptr(grad_kv), _ptr(grad_weight), N, _stream(stream, x)))
+
+
 def engram_fused_weight(wh, we, weight, stream=None) -> None:
     """weight [4,5120] fp32 = float(wh) * float(we), wh and we [4,5120] bf16 (exact)."""
     w = STREAMS * HIDDEN
@@ -286,5 +305,5 @@ def engram_gateconv_bwd(dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms
                                    _ptr(workspace), M, T, d, _stream(stream, H)))
 
 
-__all__ = ["engram_gateconv_fwd", "engram_gateconv_bwd", "engram_gateconv_bwd_workspace_bytes", "engram_gate_bwd_with_norm_weights", "engram_fused_weight", "engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
+__all__ = ["engram_gate_bwd_noalloc", "engram_gateconv_fwd", "engram_gateconv_bwd", "engram_gateconv_bwd_workspace_bytes", "engram_gate_bwd_with_norm_weights", "engram_fused_weight", "engram_gate_fwd", "engram_gate_bwd", "engram_gate_bwd_workspace_bytes", "EngramError", "lib",
            "LIB_PATH"]

@@ -113,8 +113,10 @@ static engram_status bwd_common(const void* x, const void* kv, const float* weig
                         range_of(workspace, (int64_t)engram_gate_bwd_workspace_bytes(N)),
                         range_of(grad_wh, gw), range_of(grad_we, gw)};
   if (any_overlap(in, 7, outs, 6)) return ENGRAM_ERR_OVERLAP;
+  // the first 16 N floats of the workspace are reserved; the partial rows follow
+  float* partial = static_cast<float*>(workspace) + 16 * N;
   return launched(engram::launch_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we, grad_wh,
-                                     grad_we, workspace, N, (hipStream_t)stream));
+                                     grad_we, partial, N, (hipStream_t)stream));
 }
 
 engram_status engram_gate_bwd(const void* x, const void* kv, const float* weight, const float* saved,
@@ -131,6 +133,27 @@ engram_status engram_gate_bwd_with_norm_weights(const void* x, const void* kv, c
   if (!wh) return ENGRAM_ERR_NULL;
   return bwd_common(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, wh, we, grad_wh, grad_we, workspace,
                     N, stream);
+}
+
+engram_status engram_gate_bwd_noalloc(const void* x, const void* kv, const float* weight, const float* saved,
+                                      const void* grad_out, void* grad_x, void* grad_kv, float* grad_weight, int64_t N,
+                                      void* stream) {
+  if (!x || !kv || !weight || !saved || !grad_out || !grad_x || !grad_kv || !grad_weight) return ENGRAM_ERR_NULL;
+  if (N < 1 || N > ENGRAM_NOALLOC_N_MAX || N > ENGRAM_BWD_N_MAX) return ENGRAM_ERR_N_RANGE;
+  if (N % ENGRAM_BWD_N_MULTIPLE != 0) return ENGRAM_ERR_N_MULT64;
+  if (!aligned16(x) || !aligned16(kv) || !aligned16(weight) || !aligned16(saved) || !aligned16(grad_out) ||
+      !aligned16(grad_x) || !aligned16(grad_kv) || !aligned16(grad_weight))
+    return ENGRAM_ERR_ALIGN;
+  const Range in[] = {range_of(x, N * kXRowBytes), range_of(kv, N * kKvRowBytes), range_of(weight, kWeightBytes),
+                      range_of(saved, N * kSavedRowBytes), range_of(grad_out, N * kXRowBytes)};
+  const Range outs[] = {range_of(grad_x, N * kXRowBytes), range_of(grad_kv, N * kKvRowBytes),
+                        range_of(grad_weight, kWeightBytes)};
+  if (any_overlap(in, 5, outs, 3)) return ENGRAM_ERR_OVERLAP;
+  float* partial = nullptr;
+  const hipError_t e = engram::scratch_partials(&partial);
+  if (e != hipSuccess) return launched(e);
+  return launched(engram::launch_bwd(x, kv, weight, saved, grad_out, grad_x, grad_kv, grad_weight, nullptr, nullptr,
+                                     nullptr, nullptr, partial, N, (hipStream_t)stream));
 }
 
 engram_status engram_fused_weight(const void* wh, const void* we, float* weight, void* stream) {

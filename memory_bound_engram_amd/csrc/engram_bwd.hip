@@ -51,6 +51,8 @@
 // floats are reserved for per-(token, stream) scalars and are unused by this
 // implementation; the partials start at float offset 16*N (byte 64*N, which
 // keeps 16-byte alignment).
+#include <mutex>
+
 #include "engram_device.h"
 #include "engram_launch.h"
 
@@ -341,13 +343,12 @@ hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hi
 
 hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const float* saved, const void* gout,
                       void* dx, void* dkv, float* dw, const void* wh, const void* we, float* gwh, float* gwe,
-                      void* workspace, int64_t n, hipStream_t stream) {
+                      float* partial, int64_t n, hipStream_t stream) {
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* kvp = static_cast<const uint16_t*>(kv);
   const uint16_t* gp = static_cast<const uint16_t*>(gout);
   uint16_t* dxp = static_cast<uint16_t*>(dx);
   uint16_t* dkvp = static_cast<uint16_t*>(dkv);
-  float* partial = static_cast<float*>(workspace) + 16 * n;
   const int nb = (int)(n / kTokensPerPartial);
   int nbv = nb;
   void* args1[] = {&xp, &kvp, &weight, &saved, &gp, &dxp, &dkvp, &partial, &nbv};
@@ -364,6 +365,43 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
   void* args2[] = {&cpartial, &dw, &nbv, &whp, &wep, &gwh, &gwe};
   return hipLaunchKernel(reinterpret_cast<const void*>(&engram_bwd_reduce_kernel),
                          dim3(kReduceCols4 / kReduceGroups), dim3(kReduceThreads), args2, 0, stream);
+}
+
+// ---- the allocation-free backward: partial rows in a file-scope device array ----
+//
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid allocation), the grad_weight partial rows can live in
+// a fixed array of this library instead of the caller's workspace: room for
+// the backward's largest N (8192 tokens = 128 rows of [4][5120] fp32, 10 MiB),
+// held by every GPU the library runs on until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is taken once per device with hipGetSymbolAddress (that device
+// current) and only that address is handed to the kernels.  Every call on a
+// GPU shares that GPU's array; the main kernel writes each partial row it
+// needs before the reduce reads it, so nothing carries over between calls,
+// but two calls that overlap in time on one GPU (different streams) race.
+constexpr int64_t kScratchFloats = (kMaxBwdTokens / kTokensPerPartial) * kStreams * kHidden;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_partials(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace engram

@@ -12,11 +12,21 @@ hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const 
                       float* saved, int64_t n, int grid, hipStream_t stream);
 
 // Enqueue the backward main kernel (4 x N/64 workgroups) and the grad_weight
-// reduction; with wh/we/gwh/gwe non-null the reduction also writes the
+// reduction; `partial` holds N/64 rows of [4][5120] fp32 (written, then read
+// back).  With wh/we/gwh/gwe non-null the reduction also writes the
 // product-rule gradients of weight = wh * we.
 hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const float* saved, const void* gout,
                       void* dx, void* dkv, float* dw, const void* wh, const void* we, float* gwh, float* gwe,
-                      void* workspace, int64_t n, hipStream_t stream);
+                      float* partial, int64_t n, hipStream_t stream);
+
+// The backward's largest N, and the devices the library keeps a scratch
+// address for.
+constexpr int64_t kMaxBwdTokens = 8192;
+constexpr int kMaxScratchDevices = 64;
+
+// Device address, on the current device, of the library's own partial-row
+// array (room for kMaxBwdTokens tokens); taken once per device.
+hipError_t scratch_partials(float** out);
 
 // Enqueue weight = float(wh) * float(we) for [4][5120] bf16 inputs.
 hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hipStream_t stream);

@@ -191,6 +191,48 @@ def test_status_strings():
         assert eg.lib.engram_status_string(s)
 
 
+# ---------------- the allocation-free backward (no workspace argument) ----------------
+
+def call_na(a, n):
+    return eg.lib.engram_gate_bwd_noalloc(a["x"], a["kv"], a["w"], a["sv"], a["g"], a["dx"], a["dkv"], a["dw"],
+                                          n, None)
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "sv", "g", "dx", "dkv", "dw"])
+def test_noalloc_rejects_null(field):
+    a = bwd_layout(64)
+    a[field] = None
+    assert call_na(a, 64) == eg.ERR_NULL
+
+
+@pytest.mark.parametrize("n,code", [(0, eg.ERR_N_RANGE), (-64, eg.ERR_N_RANGE), (8256, eg.ERR_N_RANGE),
+                                    (1 << 20, eg.ERR_N_RANGE), (100, eg.ERR_N_MULT64), (8191, eg.ERR_N_MULT64)])
+def test_noalloc_rejects_sizes_beyond_its_array(n, code):
+    assert call_na(bwd_layout(max(n, 64)), n) == code
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (ENGRAM_NOALLOC_\w+) (\d+)", text))
+    assert int(consts["ENGRAM_NOALLOC_N_MAX"]) == eg.NOALLOC_N_MAX == 8192
+    assert int(consts["ENGRAM_NOALLOC_SCRATCH_BYTES"]) == (8192 // 64) * 4 * 5120 * 4
+
+
+@pytest.mark.parametrize("field", ["x", "kv", "w", "sv", "g", "dx", "dkv", "dw"])
+def test_noalloc_rejects_misaligned(field):
+    a = bwd_layout(64)
+    a[field] += 8
+    assert call_na(a, 64) == eg.ERR_ALIGN
+
+
+@pytest.mark.parametrize("out,other", [("dx", "x"), ("dx", "g"), ("dkv", "kv"), ("dw", "w"), ("dw", "sv"),
+                                       ("dx", "dkv"), ("dkv", "dw")])
+def test_noalloc_rejects_overlap(out, other):
+    a = bwd_layout(64)
+    a[out] = a[other]
+    assert call_na(a, 64) == eg.ERR_OVERLAP
+
+
 # ---------------- backward with the product rule; fused weight ----------------
 
 def nw_layout(n):

@@ -162,3 +162,11 @@ def test_gateconv_backward_rejects_a_short_workspace():
     args["dv"] = meta((M, T, d), torch.float32)
     with pytest.raises(ValueError, match="dv: dtype float32"):
         eg.engram_gateconv_bwd(**args)
+
+
+def test_noalloc_backward_checks_tensors():
+    a = gate_bwd_args(64)
+    del a["workspace"]
+    a["grad_kv"] = meta((64, 25599), torch.bfloat16)
+    with pytest.raises(ValueError, match="grad_kv: .* needs at least"):
+        eg.engram_gate_bwd_noalloc(**a, N=64)
