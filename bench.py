@@ -385,6 +385,53 @@ def bench_configs(torch, synth, eg, dev, stream, with_cpu, rotate):
         print(json.dumps(line), flush=True)
 
 
+def bench_placement(torch, synth, eg, dev, stream, reps=5):
+    """The N = 1,048,512 forward (one launch, ~140 GB) under several placements
+    of its three large tensors, in one process: X, KV and out allocated
+    separately in each of three orders, and carved from one allocation.  The
+    caching allocator is emptied between placements so each gets fresh device
+    memory.  Prints one JSON line per placement (median of `reps` launches)."""
+    nl = N_LARGE
+    shapes = {"x": ((nl, 4, 5120), torch.bfloat16), "kv": ((nl, 25600), torch.bfloat16),
+              "out": ((nl, 4, 5120), torch.bfloat16)}
+    orders = [("x", "kv", "out"), ("kv", "out", "x"), ("out", "x", "kv"), "pooled"]
+    w = torch.from_numpy(synth.normal_f32(4 * 5120, SEED, synth.ID_W, 1.0, 0.1).reshape(4, 5120)).to(dev)
+    m = torch.empty(nl, dtype=torch.uint8, device=dev)
+    synth.dev_mask(m, SEED, P_MASK)
+    saved = torch.empty((nl, 4, 4), dtype=torch.float32, device=dev)
+    for order in orders:
+        torch.cuda.empty_cache()
+        t = {}
+        if order == "pooled":
+            sizes = {k: int(torch.Size(sh).numel()) for k, (sh, _) in shapes.items()}
+            pool = torch.empty(sum(sizes.values()), dtype=torch.bfloat16, device=dev)
+            off = 0
+            for k in ("x", "kv", "out"):
+                t[k] = pool[off:off + sizes[k]].view(shapes[k][0])
+                off += sizes[k]
+        else:
+            for k in order:
+                t[k] = torch.empty(shapes[k][0], dtype=shapes[k][1], device=dev)
+        synth.dev_normal_bf16(t["x"], SEED, synth.ID_X)
+        synth.dev_normal_bf16(t["kv"], SEED, synth.ID_KV)
+        for _ in range(2):
+            eg.engram_gate_fwd(t["x"], t["kv"], w, m, t["out"], saved, nl, stream=stream)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for i in range(reps):
+            ev[i][0].record(stream)
+            eg.engram_gate_fwd(t["x"], t["kv"], w, m, t["out"], saved, nl, stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+        gbps = fwd_bytes(nl) / (ms[reps // 2] * 1e-3) / 1e9
+        print(json.dumps({"placement": order if order == "pooled" else "separate, allocated " + ", ".join(order),
+                          "addresses": {k: hex(v.data_ptr()) for k, v in t.items()},
+                          "ms_median": round(ms[reps // 2], 3), "ms_all": [round(x, 3) for x in ms],
+                          "tensor_gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_GBPS, 4)}), flush=True)
+        t.clear()
+        pool = None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +449,9 @@ def main():
                          "finds its data in cache from the previous one")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the benchmark line, one line per workload configuration (0-4)")
+    ap.add_argument("--placement", action="store_true",
+                    help="instead of the benchmark line, the N=1,048,512 forward under several "
+                         "placements of its tensors (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -425,6 +475,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.placement:
+        bench_placement(torch, synth, eg, dev, torch.cuda.current_stream(dev))
+        return
     if args.configs:
         bench_configs(torch, synth, eg, dev, torch.cuda.current_stream(dev), not args.no_cpu, max(1, args.rotate))
         return

@@ -40,5 +40,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
+PROBE_BIN = os.path.join(PKG, "probe", "hbm_probe")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The HBM streaming-ceiling measurement program (not part of libengram)."""
+    tmp = PROBE_BIN + ".tmp"
+    cmd = ["hipcc", *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {PROBE_BIN}")
+    os.replace(tmp, PROBE_BIN)
+    return PROBE_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe(verbose=True))
