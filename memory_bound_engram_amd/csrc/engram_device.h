@@ -52,18 +52,36 @@ __device__ __forceinline__ float dpp(float v) {
       __builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, kBankMask, kBoundCtrl));
 }
 
+// v += the value of lane 15 of the previous row, in rows 1 and 3 only
+// (row_bcast:15, row mask 0xa); lanes of rows 0 and 2 are not written.  One
+// DPP add: the builtin form needs a zero moved in and a separate add.  The
+// s_nop gives the two wait states a DPP read of a VGPR written by the
+// previous VALU instruction needs.
+__device__ __forceinline__ float add_row_bcast15(float v) {
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+  return v;
+}
+
+// v += the value of lane 31, in rows 2 and 3 only (row_bcast:31, row mask 0xc).
+__device__ __forceinline__ float add_row_bcast31(float v) {
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(v));
+  return v;
+}
+
 // Sum over the 64 lanes of a wave; the full sum lands in lane 63 (other
 // lanes hold partial sums).  Fixed order, so the result is deterministic.
 //   quad_perm[1,0,3,2], quad_perm[2,3,0,1]  -> sums of 4
 //   row_half_mirror, row_mirror             -> sums of 16 in every lane of a row
 //   row_bcast:15 (rows 1,3), row_bcast:31 (rows 2,3) -> lane 63 holds all 64
+// (lane 63 adds, in order: its row's sum, row 2's, then lane 31's sum of rows
+// 0 and 1 -- lane 31 is in row 1, which the first broadcast does update)
 __device__ __forceinline__ float wave_sum_to_lane63(float v) {
   v += dpp<0xB1, 0xF, 0xF, true>(v);
   v += dpp<0x4E, 0xF, 0xF, true>(v);
   v += dpp<0x141, 0xF, 0xF, true>(v);
   v += dpp<0x140, 0xF, 0xF, true>(v);
-  v += dpp<0x142, 0xA, 0xF, false>(v);
-  v += dpp<0x143, 0xC, 0xF, false>(v);
+  v = add_row_bcast15(v);
+  v = add_row_bcast31(v);
   return v;
 }
 

@@ -82,7 +82,13 @@ template <class MP, bool KEEP>
 __device__ __forceinline__ void load_raw(Raw<MP>& r, const uint16_t* row, int j) {
 #pragma unroll
   for (int o = 0; o < MP::NO; ++o) r.o[o] = KEEP ? load16(row + MP::oct_col(j, o)) : load16_stream(row + MP::oct_col(j, o));
-  if constexpr (MP::PAIR) r.p = KEEP ? ld4_keep(row + MP::pair_col(j)) : ld4(row + MP::pair_col(j));
+  if constexpr (MP::PAIR) {
+    // a 32-bit byte offset from the row base, so the load takes the base in
+    // scalar registers (a column index alone gets a 64-bit vector address)
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(row) +
+                                                          (uint32_t)(2 * MP::pair_col(j)));
+    r.p = KEEP ? ld4_keep(q) : ld4(q);
+  }
 }
 
 template <class MP>
@@ -393,8 +399,11 @@ gateconv_fwd_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__
 // steps earlier, come from L2.  The step is unrolled by four, so the u and dc
 // histories are rings whose slots have fixed roles in each of the four steps;
 // the u ring holds u / w_v = vhat rrms_v.
-// LDS holds w_v and conv_w; with more than eight waves (at most 168 VGPRs a
-// thread) the conv_w tap 2 and 3 gradient accumulators move to LDS too.
+// LDS holds the combined tap weights W_i = conv_w[i] w_v, read once per step:
+// c = sum_i W_i (u / w_v)_{t-3+i} needs no multiply by w_v, and the finished
+// row needs w_v du = sum_i W_i dc_{t+3-i} rather than du itself.  With more
+// than eight waves (at most 168 VGPRs a thread) the conv_w tap 2 and 3
+// gradient accumulators move to LDS too.
 template <class MP>
 __global__ void __launch_bounds__(MP::THREADS)
 gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __restrict__ V,
@@ -403,40 +412,44 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
                          const float* __restrict__ rrv, uint16_t* __restrict__ dV, float* __restrict__ ds_out,
                          float* __restrict__ partial, int rows, int T, int chunk) {
   constexpr int d = MP::d, C = MP::C;
-  constexpr bool kLdsTaps = MP::NW > 8;  // conv_w taps 2, 3 accumulate in LDS
-  __shared__ __align__(16) float lw[(kLdsTaps ? 7 : 5) * d];  // w_v [d], conv_w [4][d] (, taps 2-3 grads [2][d])
+  // conv_w gradient taps kRegTaps..3 accumulate in LDS when more than eight
+  // waves leave a thread at most 168 VGPRs (d = 4608: taps 2 and 3, the split
+  // with the least spilling, 16 bytes a lane); all four stay in registers otherwise
+  constexpr int kRegTaps = MP::NW > 8 ? 2 : kTaps;
+  constexpr int kLdsTapPlanes = kTaps - kRegTaps;
+  // the combined tap weights W_i = conv_w[i] w_v [4][d] (, taps 2-3 grads [2][d]):
+  // c = sum_i W_i (u / w_v)_{t-3+i} and w_v du_t = sum_i W_i dc_{t+3-i} both use them
+  __shared__ __align__(16) float lw[(kTaps + kLdsTapPlanes) * d];
   __shared__ float red[2][kMaxWaves][4];
-  const float* lwv = lw;
-  const float* lcw = lw + d;
-  float* lacw = lw + 5 * d;
+  const float* lW = lw;
+  float* lacw = lw + 4 * d;
   const int j = threadIdx.x;
   const int r0 = blockIdx.x * chunk;
   const int r1 = min(r0 + chunk, rows);
   const int rb = max(r0 - (kTaps - 1), r0 - r0 % T);            // halo rows before, same sequence
   const int re = min(r1 + (kTaps - 1), ((r1 - 1) / T + 1) * T);  // rows after, same sequence
   constexpr float inv_d = 1.0f / (float)d;
-  {  // this thread's w_v and conv_w columns, plane-major (see lds_load)
-    float t[C];
-    load_cols<MP>(wv, j, t);
-    lds_store<MP>(lw, j, t);
+  {  // this thread's combined tap weights, plane-major (see lds_load)
+    float v[C], t[C];
+    load_cols<MP>(wv, j, v);
 #pragma unroll
     for (int i = 0; i < kTaps; ++i) {
       load_cols<MP>(cw + i * d, j, t);
-      lds_store<MP>(lw + (1 + i) * d, j, t);
+#pragma unroll
+      for (int e = 0; e < C; ++e) t[e] *= v[e];
+      lds_store<MP>(lw + i * d, j, t);
     }
   }
 
   float uh[kTaps][C];   // ring of u / w_v rows (vhat rrms_v)
   float dch[kTaps][C];  // ring of dc rows
-  float acw[kTaps][C];  // conv_w gradients against u / w_v (taps 2, 3 unused when in LDS)
+  float acw[kTaps][C];  // conv_w gradients against u / w_v (taps from kRegTaps on unused: in LDS)
 #pragma unroll
   for (int e = 0; e < C; ++e)
 #pragma unroll
     for (int i = 0; i < kTaps; ++i) uh[i][e] = dch[i][e] = acw[i][e] = 0.f;
-  if constexpr (kLdsTaps) {
-    lds_store<MP>(lacw, j, acw[2]);
-    lds_store<MP>(lacw + d, j, acw[3]);
-  }
+#pragma unroll
+  for (int i = kRegTaps; i < kTaps; ++i) lds_store<MP>(lacw + (i - kRegTaps) * d, j, acw[i]);
 
   Raw<MP> nv, ng;  // slot N: vhat, dY of the newest row
   Raw<MP> lv;      // slot L: v of the finished row
@@ -486,42 +499,39 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
     const float rvn = tau < re ? rrv[tau] : 0.f;  // u = 0 past the rows this chunk needs
 #pragma unroll
     for (int e = 0; e < C; ++e) uh[k0][e] = vn[e] * rvn;
+    // the combined tap weights, for the newest row's c and the finished row's du
+    float w0[C], w1[C], w2[C], w3[C];
+    lds_load<MP>(lW, j, w0);
+    lds_load<MP>(lW + d, j, w1);
+    lds_load<MP>(lW + 2 * d, j, w2);
+    lds_load<MP>(lW + 3 * d, j, w3);
     if (tau >= r0 && tau < re) {
-      float w0[C], w1[C], w2[C], w3[C], g2[C], g3[C], w4[C];
-      lds_load<MP>(lwv, j, w4);
-      lds_load<MP>(lcw, j, w0);
-      lds_load<MP>(lcw + d, j, w1);
-      lds_load<MP>(lcw + 2 * d, j, w2);
-      lds_load<MP>(lcw + 3 * d, j, w3);
-      if constexpr (kLdsTaps) {
-        lds_load<MP>(lacw, j, g2);
-        lds_load<MP>(lacw + d, j, g3);
-      }
+      float gl[kLdsTapPlanes > 0 ? kLdsTapPlanes : 1][C];  // the LDS-held taps of this step
+#pragma unroll
+      for (int i = 0; i < kLdsTapPlanes; ++i) lds_load<MP>(lacw + i * d, j, gl[i]);
 #pragma unroll
       for (int x = 0; x < C; ++x) {
         float c = w0[x] * uh[k1][x];
         c = fmaf(w1[x], uh[k2][x], c);
         c = fmaf(w2[x], uh[k3][x], c);
-        c = fmaf(w3[x], uh[k0][x], c) * w4[x];
+        c = fmaf(w3[x], uh[k0][x], c);
         const float sg = sigmoidf_(c);
         const float dc = gn[x] * (sg * fmaf(c, 1.0f - sg, 1.0f));
         dch[k0][x] = dc;
         if (tau < r1) {  // dc of rows past the chunk enter no gradient
-          acw[0][x] = fmaf(dc, uh[k1][x], acw[0][x]);
-          acw[1][x] = fmaf(dc, uh[k2][x], acw[1][x]);
-          if constexpr (kLdsTaps) {
-            g2[x] = fmaf(dc, uh[k3][x], g2[x]);
-            g3[x] = fmaf(dc, uh[k0][x], g3[x]);
-          } else {
-            acw[2][x] = fmaf(dc, uh[k3][x], acw[2][x]);
-            acw[3][x] = fmaf(dc, uh[k0][x], acw[3][x]);
+          // tap i pairs dc_tau with u of row tau - 3 + i: ring slots k1, k2, k3, k0
+          const float up[kTaps] = {uh[k1][x], uh[k2][x], uh[k3][x], uh[k0][x]};
+#pragma unroll
+          for (int i = 0; i < kTaps; ++i) {
+            if (i < kRegTaps)
+              acw[i][x] = fmaf(dc, up[i], acw[i][x]);
+            else
+              gl[i - kRegTaps][x] = fmaf(dc, up[i], gl[i - kRegTaps][x]);
           }
         }
       }
-      if constexpr (kLdsTaps) {
-        lds_store<MP>(lacw, j, g2);
-        lds_store<MP>(lacw + d, j, g3);
-      }
+#pragma unroll
+      for (int i = 0; i < kLdsTapPlanes; ++i) lds_store<MP>(lacw + i * d, j, gl[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < C; ++e) dch[k0][e] = 0.f;
@@ -540,25 +550,19 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
       float vh[C], gy[C];
       unpack_raw<MP>(fv, vh);
       unpack_raw<MP>(fg, gy);
-      // du_t = sum_i conv_w[i] dc_{t+3-i}; dc of rows past the end of t's
+      // w_v du_t = sum_i W_i dc_{t+3-i}; dc of rows past the end of t's
       // sequence count as 0 (they belong to the next sequence).  With
       // A = dY + rrms_v w_v du, dvhat = A - rrms_v c1 vhat (c1 = rrms_v^2 S1 / d):
       //   S1 = sum du w_v vhat,  dalpha = sum A v - rrms_v c1 sum vhat v
-      float w0[C], w1[C], w2[C], w3[C], wvq[C];
-      lds_load<MP>(lcw, j, w0);
-      lds_load<MP>(lcw + d, j, w1);
-      lds_load<MP>(lcw + 2 * d, j, w2);
-      lds_load<MP>(lcw + 3 * d, j, w3);
-      lds_load<MP>(lwv, j, wvq);
       float s[3];
-      float A[C], du[C];
-      if (ahead >= 3) {
+      float A[C], dwu[C];
+      if (__builtin_expect(ahead >= 3, 1)) {
 #pragma unroll
         for (int x = 0; x < C; ++x) {
           float dd = w3[x] * dch[k1][x];
           dd = fmaf(w2[x], dch[k2][x], dd);
           dd = fmaf(w1[x], dch[k3][x], dd);
-          du[x] = fmaf(w0[x], dch[k0][x], dd);
+          dwu[x] = fmaf(w0[x], dch[k0][x], dd);
         }
       } else {  // the last rows of a sequence (rare): rows past its end are skipped
 #pragma unroll
@@ -566,13 +570,12 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
           float dd = w3[x] * dch[k1][x];
           if (ahead >= 1) dd = fmaf(w2[x], dch[k2][x], dd);
           if (ahead >= 2) dd = fmaf(w1[x], dch[k3][x], dd);
-          du[x] = dd;
+          dwu[x] = dd;
         }
       }
 #pragma unroll
       for (int x = 0; x < C; ++x) {
-        const float dd = du[x];
-        const float dw = dd * wvq[x];
+        const float dw = dwu[x];  // w_v du
         A[x] = fmaf(rv, dw, gy[x]);
         const float p0 = dw * vh[x], p1 = A[x] * v[x], p2 = vh[x] * v[x];
         s[0] = x == 0 ? p0 : s[0] + p0;
@@ -605,17 +608,15 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
 
   // this workgroup's partials: rows 1..4 (the conv_w taps, against u / w_v) of its [5][d] block
   float* p = partial + (int64_t)blockIdx.x * kPartRows * d;
-  store_cols<MP>(p + d, j, acw[0]);
-  store_cols<MP>(p + 2 * d, j, acw[1]);
-  if constexpr (kLdsTaps) {
-    float g[C];
-    lds_load<MP>(lacw, j, g);
-    store_cols<MP>(p + 3 * d, j, g);
-    lds_load<MP>(lacw + d, j, g);
-    store_cols<MP>(p + 4 * d, j, g);
-  } else {
-    store_cols<MP>(p + 3 * d, j, acw[2]);
-    store_cols<MP>(p + 4 * d, j, acw[3]);
+#pragma unroll
+  for (int i = 0; i < kTaps; ++i) {
+    if (i < kRegTaps) {
+      store_cols<MP>(p + (1 + i) * d, j, acw[i]);
+    } else {
+      float g[C];
+      lds_load<MP>(lacw + (i - kRegTaps) * d, j, g);
+      store_cols<MP>(p + (1 + i) * d, j, g);
+    }
   }
 }
 

@@ -615,6 +615,15 @@ int engram_oracle_weight_grads(int64_t count, const double *dw, const uint16_t *
  *   G5  c[t] = sum_{i<4} conv_w[i] u[t-3+i], causal within each sequence m,
  *       zero history before t = 0, dilation 1 (the op has no dilation).
  *   G6  Y = SiLU(c) + vhat, SiLU(c) = c sigmoid(c).
+ * Parity unpinned on two points: the page fixes neither the 1/sqrt(d) in G2
+ * (it names a scalar gate from the normalised H and k, nothing about a scale;
+ * the scaled dot product is the usual form of such a gate, and without it the
+ * logit grows sqrt(d) times and alpha saturates at 0 or 1 on most rows) nor
+ * which tensor the "+ residual" of G6 adds (it lists SiLU + residual among the
+ * op's stages, and separately says the caller adds Y to H; vhat is the one
+ * op-internal tensor of matching shape -- the alternative Y = SiLU(c) drops
+ * the vhat term from Y and from the gradient of vhat).  The tests pin the
+ * oracle to these readings, not to the page.
  * Layout: H, k, v, Y, vhat, dY, dH, dk, dv [M][T][d]; alpha, rrms_* [M][T];
  * w_h, w_v [d]; conv_w [4][d].
  *
