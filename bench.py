@@ -432,6 +432,89 @@ def bench_placement(torch, synth, eg, dev, stream, reps=5):
         pool = None
 
 
+def bench_same_buffers(torch, synth, eg, dev, stream, placements=3, reps=20):
+    """The gate's kernels against plain streams of exactly their traffic, over
+    the same buffers in the same process: for each of `placements` fresh
+    allocations of the N = 8192 step's four buffer sets, the forward, a plain
+    stream X, KV -> out, the backward, and a plain stream X, KV, grad_out ->
+    grad_x, grad_kv (the probe library's kernels: whole tokens per 512-thread
+    workgroup in several dealings and grids, and the backward's own split --
+    a quarter of every row per 256-thread workgroup), interleaved call by
+    call; one JSON
+    line per placement with the median microseconds of each and the rates over
+    each one's own bytes."""
+    import ctypes
+    plib = ctypes.CDLL(os.path.join(ROOT, "memory_bound_engram_amd", "probe", "libengram_probe.so"))
+    plib.probe_stream.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
+    plib.probe_stream.restype = ctypes.c_int
+    n, R = N_STEP, 4
+    stream_fwd_bytes = (40960 + 51200 + 40960) * n
+    stream_bwd_bytes = (40960 + 51200 + 40960 + 40960 + 51200) * n
+
+    def probe(shape, ins, outs, grid, deal):
+        a_in = (ctypes.c_void_p * len(ins))(*[t.data_ptr() for t in ins])
+        a_out = (ctypes.c_void_p * len(outs))(*[t.data_ptr() for t in outs])
+        rc = plib.probe_stream(shape.encode(), a_in, a_out, n, grid, deal, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_stream({shape}) returned {rc}")
+
+    for pl in range(placements):
+        torch.cuda.empty_cache()
+        sets = []
+        for _ in range(R):
+            x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
+            sets.append(dict(x=x, kv=kv, w=w, m=m, g=g, out=torch.empty_like(x),
+                             saved=torch.empty((n, 4, 4), dtype=torch.float32, device=dev),
+                             gx=torch.empty_like(x), gkv=torch.empty_like(kv),
+                             gw=torch.empty((4, 5120), dtype=torch.float32, device=dev),
+                             ws=torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev)))
+        calls = {
+            "gate_fwd": lambda b: eg.engram_gate_fwd(b["x"], b["kv"], b["w"], b["m"], b["out"], b["saved"], n,
+                                                     stream=stream),
+            "stream_fwd_lockstep1024": lambda b: probe("fwd", [b["x"], b["kv"]], [b["out"]], 1024, 0),
+            "stream_fwd_bands256": lambda b: probe("fwd", [b["x"], b["kv"]], [b["out"]], 256, 2),
+            "gate_bwd": lambda b: eg.engram_gate_bwd(b["x"], b["kv"], b["w"], b["saved"], b["g"], b["gx"], b["gkv"],
+                                                     b["gw"], b["ws"], n, stream=stream),
+            "stream_bwd_lockstep1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 0),
+            "stream_bwd_lockstep256": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 256, 0),
+            "stream_bwd_lockstep2048": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 2048, 0),
+            "stream_bwd_chunked1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 1),
+            "stream_bwd_bands256": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 256, 2),
+            "stream_bwd_quarters1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 3),
+            "stream_bwd_quarters2048": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 2048, 3),
+            "stream_bwd_quarters4096": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 4096, 3),
+        }
+        for b in sets:  # the backward needs the forward's saved state
+            calls["gate_fwd"](b)
+        for i in range(2 * R):
+            for f in calls.values():
+                f(sets[i % R])
+        torch.cuda.synchronize()
+        ev = {k: [] for k in calls}
+        for i in range(reps):
+            b = sets[i % R]
+            for k, f in calls.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                f(b)
+                e1.record(stream)
+                ev[k].append((e0, e1))
+        torch.cuda.synchronize()
+        us = {k: sorted(e0.elapsed_time(e1) for e0, e1 in v)[len(v) // 2] * 1e3 for k, v in ev.items()}
+        own = {"gate_fwd": fwd_bytes(n), "gate_bwd": bwd_bytes(n)}
+        line = {"placement": pl, "tokens": n, "buffer_sets_rotated": R, "reps": reps,
+                "us": {k: round(v, 2) for k, v in us.items()},
+                "tb_s_own_bytes": {k: round((own.get(k) or (stream_fwd_bytes if "fwd" in k else stream_bwd_bytes))
+                                            / (v * 1e-6) / 1e12, 3) for k, v in us.items()},
+                "gate_fwd_over_best_stream": round(min(us["stream_fwd_lockstep1024"], us["stream_fwd_bands256"])
+                                                   / us["gate_fwd"], 4),
+                "gate_bwd_over_best_stream": round(min(v for k, v in us.items() if k.startswith("stream_bwd"))
+                                                   / us["gate_bwd"], 4)}
+        print(json.dumps(line), flush=True)
+        sets.clear()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,6 +535,9 @@ def main():
     ap.add_argument("--placement", action="store_true",
                     help="instead of the benchmark line, the N=1,048,512 forward under several "
                          "placements of its tensors (one JSON line each)")
+    ap.add_argument("--same-buffers", action="store_true",
+                    help="instead of the benchmark line, the gate's kernels against plain streams of the "
+                         "same traffic over the same buffers, for three fresh placements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -475,6 +561,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.same_buffers:
+        bench_same_buffers(torch, synth, eg, dev, torch.cuda.current_stream(dev))
+        return
     if args.placement:
         bench_placement(torch, synth, eg, dev, torch.cuda.current_stream(dev))
         return

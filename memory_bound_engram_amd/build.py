@@ -56,6 +56,23 @@ def build_probe(verbose: bool = False) -> str:
     return PROBE_BIN
 
 
+PROBE_LIB_SRC = os.path.join(PKG, "probe", "stream_lib.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libengram_probe.so")
+
+
+def build_probe_lib(verbose: bool = False) -> str:
+    """The probe's streaming kernels as a shared library (bench.py --same-buffers)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = ["hipcc", *HIPCC_FLAGS, "-o", tmp, PROBE_LIB_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {PROBE_LIB}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     print(build_probe(verbose=True))
+    print(build_probe_lib(verbose=True))

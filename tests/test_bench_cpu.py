@@ -66,16 +66,20 @@ def test_recorded_traffic_invalidated_by_a_source_change(tmp_path):
     (root / "memory_bound_engram_amd" / "csrc").mkdir(parents=True)
     (root / "profiles").mkdir()
     shutil.copy(os.path.join(ROOT, "bench.py"), root / "bench.py")
-    shutil.copy(os.path.join(ROOT, "profiles", "traffic.json"), root / "profiles" / "traffic.json")
     for name in ("engram_device.h", "engram_fwd.hip", "engram_bwd.hip", "engram_gateconv.hip", "engram_api.cpp"):
         shutil.copy(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", name),
                     root / "memory_bound_engram_amd" / "csrc" / name)
     b = load_bench(str(root))
-    assert b.recorded_traffic("bwd") is not None
+    # a record taken on exactly these sources, whatever the committed one's age
+    rec = {k: {"source_hash": b.kernel_source_hash(k), "bytes_per_launch": 1000 + i}
+           for i, k in enumerate(b.KERNEL_SOURCES)}
+    with open(root / "profiles" / "traffic.json", "w") as f:
+        json.dump(rec, f)
+    assert b.recorded_traffic("bwd") == rec["bwd"]["bytes_per_launch"]
     with open(root / "memory_bound_engram_amd" / "csrc" / "engram_bwd.hip", "a") as f:
         f.write("\n// edited\n")
     assert b.recorded_traffic("bwd") is None
-    assert b.recorded_traffic("fwd") is not None  # other kernels keep their record
+    assert b.recorded_traffic("fwd") == rec["fwd"]["bytes_per_launch"]  # other kernels keep their record
 
 
 def test_more_than_one_gpu_is_refused():
