@@ -432,23 +432,26 @@ def bench_placement(torch, synth, eg, dev, stream, reps=5):
         pool = None
 
 
-def bench_same_buffers(torch, synth, eg, dev, stream, placements=3, reps=20):
+def bench_same_buffers(torch, synth, eg, dev, stream, placements=3, reps=20, sets_per_placement=5):
     """The gate's kernels against plain streams of exactly their traffic, over
-    the same buffers in the same process: for each of `placements` fresh
-    allocations of the N = 8192 step's four buffer sets, the forward, a plain
-    stream X, KV -> out, the backward, and a plain stream X, KV, grad_out ->
-    grad_x, grad_kv (the probe library's kernels: whole tokens per 512-thread
-    workgroup in several dealings and grids, and the backward's own split --
-    a quarter of every row per 256-thread workgroup), interleaved call by
-    call; one JSON
-    line per placement with the median microseconds of each and the rates over
-    each one's own bytes."""
+    the same buffers in the same process (the probe library's kernels: whole
+    tokens per 512-thread workgroup in lockstep over 256 or 1024 workgroups,
+    and the backward's own split -- a quarter of every row per 256-thread
+    workgroup).  Each placement allocates `sets_per_placement` fresh buffer
+    sets of the N = 8192 step.  Two contexts, medians of `reps` calls each:
+      cold: every call runs on a different buffer set than the call before it,
+        so none reads what the previous call left in the 256 MB last-level
+        cache (back-to-back calls on the same buffers gain up to ~15% from it,
+        by an amount that depends on the order of both calls);
+      after_fwd: the gate's forward on a set, then the timed call on the same
+        set -- the benchmark step's context for the backward.
+    One JSON line per placement."""
     import ctypes
     plib = ctypes.CDLL(os.path.join(ROOT, "memory_bound_engram_amd", "probe", "libengram_probe.so"))
     plib.probe_stream.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                                   ctypes.c_int, ctypes.c_void_p]
     plib.probe_stream.restype = ctypes.c_int
-    n, R = N_STEP, 4
+    n = N_STEP
     stream_fwd_bytes = (40960 + 51200 + 40960) * n
     stream_bwd_bytes = (40960 + 51200 + 40960 + 40960 + 51200) * n
 
@@ -459,58 +462,76 @@ def bench_same_buffers(torch, synth, eg, dev, stream, placements=3, reps=20):
         if rc != 0:
             raise RuntimeError(f"probe_stream({shape}) returned {rc}")
 
+    def sfwd(grid):
+        return lambda b: probe("fwd", [b["x"], b["kv"]], [b["out"]], grid, 0)
+
+    def sbwd(grid, deal):
+        return lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], grid, deal)
+
+    gate_fwd = lambda b: eg.engram_gate_fwd(b["x"], b["kv"], b["w"], b["m"], b["out"], b["saved"], n, stream=stream)
+    gate_bwd = lambda b: eg.engram_gate_bwd(b["x"], b["kv"], b["w"], b["saved"], b["g"], b["gx"], b["gkv"], b["gw"],
+                                            b["ws"], n, stream=stream)
+    calls = {"gate_fwd": gate_fwd, "stream_fwd_lockstep256": sfwd(256), "stream_fwd_lockstep1024": sfwd(1024),
+             "gate_bwd": gate_bwd, "stream_bwd_lockstep256": sbwd(256, 0), "stream_bwd_lockstep1024": sbwd(1024, 0),
+             "stream_bwd_quarters4096": sbwd(4096, 3)}
+    after = ["gate_bwd", "stream_bwd_lockstep256", "stream_bwd_lockstep1024"]
+    own = {"gate_fwd": fwd_bytes(n), "gate_bwd": bwd_bytes(n)}
+
+    def timed(f, b, pre=None):
+        if pre is not None:
+            pre(b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        f(b)
+        e1.record(stream)
+        return e0, e1
+
+    def medians(ev):
+        return {k: round(sorted(a.elapsed_time(z) for a, z in v)[len(v) // 2] * 1e3, 2) for k, v in ev.items()}
+
     for pl in range(placements):
         torch.cuda.empty_cache()
         sets = []
-        for _ in range(R):
+        for _ in range(sets_per_placement):
             x, kv, w, m, g = make_inputs(torch, synth, n, dev, grad=True)
             sets.append(dict(x=x, kv=kv, w=w, m=m, g=g, out=torch.empty_like(x),
                              saved=torch.empty((n, 4, 4), dtype=torch.float32, device=dev),
                              gx=torch.empty_like(x), gkv=torch.empty_like(kv),
                              gw=torch.empty((4, 5120), dtype=torch.float32, device=dev),
                              ws=torch.empty(eg.engram_gate_bwd_workspace_bytes(n), dtype=torch.uint8, device=dev)))
-        calls = {
-            "gate_fwd": lambda b: eg.engram_gate_fwd(b["x"], b["kv"], b["w"], b["m"], b["out"], b["saved"], n,
-                                                     stream=stream),
-            "stream_fwd_lockstep1024": lambda b: probe("fwd", [b["x"], b["kv"]], [b["out"]], 1024, 0),
-            "stream_fwd_bands256": lambda b: probe("fwd", [b["x"], b["kv"]], [b["out"]], 256, 2),
-            "gate_bwd": lambda b: eg.engram_gate_bwd(b["x"], b["kv"], b["w"], b["saved"], b["g"], b["gx"], b["gkv"],
-                                                     b["gw"], b["ws"], n, stream=stream),
-            "stream_bwd_lockstep1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 0),
-            "stream_bwd_lockstep256": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 256, 0),
-            "stream_bwd_lockstep2048": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 2048, 0),
-            "stream_bwd_chunked1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 1),
-            "stream_bwd_bands256": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 256, 2),
-            "stream_bwd_quarters1024": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 1024, 3),
-            "stream_bwd_quarters2048": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 2048, 3),
-            "stream_bwd_quarters4096": lambda b: probe("bwd", [b["x"], b["kv"], b["g"]], [b["gx"], b["gkv"]], 4096, 3),
-        }
         for b in sets:  # the backward needs the forward's saved state
-            calls["gate_fwd"](b)
-        for i in range(2 * R):
-            for f in calls.values():
-                f(sets[i % R])
-        torch.cuda.synchronize()
-        ev = {k: [] for k in calls}
-        for i in range(reps):
-            b = sets[i % R]
+            gate_fwd(b)
+        c = 0  # call counter: call c runs on set c mod R, never the previous call's set
+        R = len(sets)
+        cold = {k: [] for k in calls}
+        for i in range(2 + reps):
             for k, f in calls.items():
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                f(b)
-                e1.record(stream)
-                ev[k].append((e0, e1))
+                pair = timed(f, sets[c % R])
+                c += 1
+                if i >= 2:
+                    cold[k].append(pair)
+        post = {k: [] for k in after}
+        for i in range(2 + reps):
+            for k in after:
+                pair = timed(calls[k], sets[c % R], pre=gate_fwd)
+                c += 1
+                if i >= 2:
+                    post[k].append(pair)
         torch.cuda.synchronize()
-        us = {k: sorted(e0.elapsed_time(e1) for e0, e1 in v)[len(v) // 2] * 1e3 for k, v in ev.items()}
-        own = {"gate_fwd": fwd_bytes(n), "gate_bwd": bwd_bytes(n)}
-        line = {"placement": pl, "tokens": n, "buffer_sets_rotated": R, "reps": reps,
-                "us": {k: round(v, 2) for k, v in us.items()},
-                "tb_s_own_bytes": {k: round((own.get(k) or (stream_fwd_bytes if "fwd" in k else stream_bwd_bytes))
-                                            / (v * 1e-6) / 1e12, 3) for k, v in us.items()},
-                "gate_fwd_over_best_stream": round(min(us["stream_fwd_lockstep1024"], us["stream_fwd_bands256"])
-                                                   / us["gate_fwd"], 4),
-                "gate_bwd_over_best_stream": round(min(v for k, v in us.items() if k.startswith("stream_bwd"))
-                                                   / us["gate_bwd"], 4)}
+        us_cold, us_after = medians(cold), medians(post)
+
+        def rate(k, v):
+            return round((own.get(k) or (stream_fwd_bytes if "fwd" in k else stream_bwd_bytes)) / (v * 1e-6) / 1e12, 3)
+
+        best_fwd = min(v for k, v in us_cold.items() if k.startswith("stream_fwd"))
+        best_bwd = min(v for k, v in us_cold.items() if k.startswith("stream_bwd"))
+        best_bwd_after = min(v for k, v in us_after.items() if k.startswith("stream_bwd"))
+        line = {"placement": pl, "tokens": n, "buffer_sets": R, "reps": reps,
+                "cold_us": us_cold, "cold_tb_s_own_bytes": {k: rate(k, v) for k, v in us_cold.items()},
+                "after_fwd_us": us_after,
+                "gate_fwd_vs_best_stream_cold": round(best_fwd / us_cold["gate_fwd"], 4),
+                "gate_bwd_vs_best_stream_cold": round(best_bwd / us_cold["gate_bwd"], 4),
+                "gate_bwd_vs_best_stream_after_fwd": round(best_bwd_after / us_after["gate_bwd"], 4)}
         print(json.dumps(line), flush=True)
         sets.clear()
 
@@ -537,7 +558,8 @@ def main():
                          "placements of its tensors (one JSON line each)")
     ap.add_argument("--same-buffers", action="store_true",
                     help="instead of the benchmark line, the gate's kernels against plain streams of the "
-                         "same traffic over the same buffers, for three fresh placements")
+                         "same traffic over the same buffers (cold, and the backward after the forward), "
+                         "for three fresh placements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")

@@ -24,12 +24,15 @@
 // handles slot u's tokens and vectors h + 2i (i = 0..4) of the 640 16-byte
 // vectors of a stream row.  Rows and tokens: up to N = 4096 there are N/64
 // rows of 64 tokens; above that (when 256 divides N) 64 rows of N/64 tokens,
-// so that the 256 workgroups are all resident at once, one per CU.  At each
-// step the workgroups of all rows together take one band of rows * 4
-// consecutive tokens, and the steps visit the bands eight apart (0, 8, 16,
-// ..., then 1, 9, ...): streaming the tensors in that order measured 6-14%
-// faster than band after band (and more steadily than four apart).  The dg partials of the two half-row waves of a token
-// meet in LDS (one barrier per step).  grad_value for vector pair i (columns
+// so that the 256 workgroups are all resident at once, one per CU.  At step
+// jj the workgroups of all rows together take band jj, the rows * 4
+// consecutive tokens from jj * rows * 4 (slot u of row b: token
+// (jj * 4 + u) * rows + b), so the chip walks the tensors front to back.
+// Other orders measured on MI355X (bands visited four or eight apart, a
+// random band order, a workgroup's slots on consecutive tokens, two rounds of
+// 128 rows) came within 1% of this one, timed either cold or right after the
+// forward on the same buffers.  The dg partials of the two half-row waves of a
+// token meet in LDS (one barrier per step).  grad_value for vector pair i (columns
 // of vectors 2i, 2i+1) is written by the stream-i workgroup for i < 4 and, for
 // i = 4, by one stream workgroup chosen by (step + slot) mod 4, so every element
 // is written once and the extra grad_out reads stay balanced.  The weight row
@@ -62,7 +65,6 @@
 namespace engram {
 
 constexpr int kBwdVecs = kRowVecs / 128;              // 5 vectors per lane (half a row)
-constexpr int kBandStride = 8;                        // band order of the main kernel's steps (when it divides them)
 
 constexpr int kBwdSlots = 4;                          // token slots per workgroup
 
@@ -101,17 +103,10 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   // the saved row (gate, dot, rstd_X, rstd_key of each stream; 64 bytes) of
   // this slot's next token, fetched one token ahead through the scalar cache
   // (the token index is wave-uniform), so no wait on it stalls the vector loads
-  // At step jj the workgroups of all rows together take one band of
-  // rows * kBwdSlots consecutive tokens -- slot u of row b the token
-  // band * rows * kBwdSlots + u * rows + b -- and the steps visit the bands
-  // kBandStride apart (0, 8, 16, ..., then 1, 9, ...) rather than one after
-  // another, when kBandStride divides the steps (band after band otherwise).
-  const int P = steps % kBandStride == 0 ? steps / kBandStride : steps;
-  const int stride = steps % kBandStride == 0 ? kBandStride : 1;
-  auto band = [&](int jj) { return (jj % P) * stride + jj / P; };
-  auto token = [&](int jj) {
-    return __builtin_amdgcn_readfirstlane((band(jj) * kBwdSlots + u) * rows + (int)b);
-  };
+  // At step jj the workgroups of all rows together take the band of
+  // rows * kBwdSlots consecutive tokens from jj * rows * kBwdSlots: slot u of
+  // row b the token (jj * kBwdSlots + u) * rows + b.
+  auto token = [&](int jj) { return __builtin_amdgcn_readfirstlane((jj * kBwdSlots + u) * rows + (int)b); };
   const f32x4* saved4 = reinterpret_cast<const f32x4*>(saved);
   f32x4 svn[kStreams];
   {
