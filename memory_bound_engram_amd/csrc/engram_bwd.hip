@@ -30,7 +30,7 @@
 // (jj * 4 + u) * rows + b), so the chip walks the tensors front to back.
 // Other orders measured on MI355X (bands visited four or eight apart, a
 // random band order, a workgroup's slots on consecutive tokens, two rounds of
-// 128 rows) came within 1% of this one, timed either cold or right after the
+// 128 rows) came within 1.5% of this one, timed either cold or right after the
 // forward on the same buffers.  The dg partials of the two half-row waves of a
 // token meet in LDS (one barrier per step).  grad_value for vector pair i (columns
 // of vectors 2i, 2i+1) is written by the stream-i workgroup for i < 4 and, for
@@ -67,6 +67,14 @@ namespace engram {
 constexpr int kBwdVecs = kRowVecs / 128;              // 5 vectors per lane (half a row)
 
 constexpr int kBwdSlots = 4;                          // token slots per workgroup
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// c + a.lo b.lo + a.hi b.hi for two packed bf16 pairs (one v_dot2 instruction;
+// each bf16 product is exact in fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
 
 // rows = partial rows (workgroups per stream), steps = tokens per slot:
 // rows * kBwdSlots * steps = N.
@@ -186,17 +194,19 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
     const float g = own[0], dot = own[1];
     const float rx = own[2], rk = own[3];
 
-    float p = 0.f;
+    // this lane's part of dg = sum_j G_j v_j, on the packed bf16 pairs, in two
+    // independent chains
+    float p0 = 0.f, p1 = 0.f;
     if (fl.live) {
 #pragma unroll
       for (int v = 0; v < kBwdVecs; ++v)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          p = fmaf(bf_lo(L.g[v][q]), bf_lo(L.v[v][q]), p);
-          p = fmaf(bf_hi(L.g[v][q]), bf_hi(L.v[v][q]), p);
+        for (int q = 0; q < 4; q += 2) {
+          p0 = dot2_bf16(L.g[v][q], L.v[v][q], p0);
+          p1 = dot2_bf16(L.g[v][q + 1], L.v[v][q + 1], p1);
         }
     }
-    p = wave_sum_to_lane63(p);
+    float p = wave_sum_to_lane63(p0 + p1);
     if (lane == 63) red[buf][u][h] = p;
     __syncthreads();
     const float dg = red[buf][u][0] + red[buf][u][1];
@@ -233,8 +243,9 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
             const float gx = hh ? bf_hi(L.g[v][q]) : bf_lo(L.g[v][q]);
             const float xx = hh ? bf_hi(L.x[v][q]) : bf_lo(L.x[v][q]);
             const float kk = hh ? bf_hi(L.k[v][q]) : bf_lo(L.k[v][q]);
-            rdx[hh] = fmaf(-cb, xx, fmaf(ca, wv[e] * kk, gx));
-            rdk[hh] = fmaf(-ce, kk, ca * (wv[e] * xx));
+            const float cw = ca * wv[e];  // a w_j, shared by grad_x and grad_key
+            rdx[hh] = fmaf(-cb, xx, fmaf(cw, kk, gx));
+            rdk[hh] = fmaf(-ce, kk, cw * xx);
             acc[v][e] = fmaf(ca, xx * kk, acc[v][e]);
           }
           ox[v][q] = pack_bf16x2(rdx[0], rdx[1]);
