@@ -49,8 +49,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // j starts at 8j + 8 THREADS o: 16-byte accesses, one wave instruction moves
 // 1 KB contiguous of bf16) and, when C % 8 == 2, one pair of 2 columns
 // starting at 8 THREADS (C/8) + 2j (256 contiguous bytes per wave
-// instruction).  Element x < C of a thread is element x % 8 of octet x / 8,
-// or element x - 8 NO of the pair.  Wide accesses keep the vector-memory
+// instruction), or, when C % 8 == 1, one single column at 8 THREADS (C/8) + j
+// (128 contiguous bytes per wave instruction).  Element x < C of a thread is
+// element x % 8 of octet x / 8, or element x - 8 NO of the pair or single.  Wide accesses keep the vector-memory
 // instructions per row few: a workgroup can have at most 63 of them in flight
 // per wave, and the row prefetch needs that headroom.
 template <int THREADS_, int C_>
@@ -58,18 +59,20 @@ struct ColMap {
   static constexpr int THREADS = THREADS_, C = C_, d = THREADS_ * C_;
   static constexpr int NO = C_ / 8;
   static constexpr bool PAIR = (C_ % 8) == 2;
+  static constexpr bool SINGLE = (C_ % 8) == 1;
   static constexpr int NW = THREADS_ / 64;
-  static_assert(C_ % 8 == 0 || C_ % 8 == 2, "columns per thread: octets and at most one pair");
+  static_assert(C_ % 8 == 0 || C_ % 8 == 2 || C_ % 8 == 1, "columns per thread: octets and at most one pair or single");
   static_assert(THREADS_ % 64 == 0 && NW >= 1 && NW <= kMaxWaves, "whole waves, at most ten");
   __device__ static constexpr int oct_col(int j, int o) { return 8 * j + 8 * THREADS_ * o; }
   __device__ static constexpr int pair_col(int j) { return 8 * THREADS_ * NO + 2 * j; }
+  __device__ static constexpr int single_col(int j) { return 8 * THREADS_ * NO + j; }
 };
 
 // Raw bf16 of one thread's C columns of one row.
 template <class MP>
 struct Raw {
   u32x4 o[MP::NO];
-  uint32_t p;  // the pair; unused (and dead) unless MP::PAIR
+  uint32_t p;  // the pair, or the single column in the low half; unused (and dead) otherwise
 };
 
 __device__ __forceinline__ uint32_t ld4(const uint16_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)); }
@@ -89,6 +92,11 @@ __device__ __forceinline__ void load_raw(Raw<MP>& r, const uint16_t* row, int j)
                                                           (uint32_t)(2 * MP::pair_col(j)));
     r.p = KEEP ? ld4_keep(q) : ld4(q);
   }
+  if constexpr (MP::SINGLE) {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(row) +
+                                                          (uint32_t)(2 * MP::single_col(j)));
+    r.p = KEEP ? (uint32_t)*q : (uint32_t)__builtin_nontemporal_load(q);
+  }
 }
 
 template <class MP>
@@ -104,6 +112,7 @@ __device__ __forceinline__ void unpack_raw(const Raw<MP>& r, float* f) {
     f[8 * MP::NO] = bf_lo(r.p);
     f[8 * MP::NO + 1] = bf_hi(r.p);
   }
+  if constexpr (MP::SINGLE) f[8 * MP::NO] = bf_lo(r.p);
 }
 
 // bf16 round-to-nearest-even stores of one row.
@@ -117,6 +126,8 @@ __device__ __forceinline__ void store_row(uint16_t* row, const float* f, int j) 
     store16_stream(row + MP::oct_col(j, o), w);
   }
   if constexpr (MP::PAIR) st4(row + MP::pair_col(j), pack_bf16x2(f[8 * MP::NO], f[8 * MP::NO + 1]));
+  if constexpr (MP::SINGLE)
+    __builtin_nontemporal_store((uint16_t)(pack_bf16x2(f[8 * MP::NO], 0.0f) & 0xffffu), row + MP::single_col(j));
 }
 
 // fp32 per-column vectors (weights, accumulators) in global memory or LDS.
@@ -135,6 +146,7 @@ __device__ __forceinline__ void load_cols(const float* base, int j, float* f) {
     f[8 * MP::NO] = b[0];
     f[8 * MP::NO + 1] = b[1];
   }
+  if constexpr (MP::SINGLE) f[8 * MP::NO] = base[MP::single_col(j)];
 }
 
 template <class MP>
@@ -147,6 +159,7 @@ __device__ __forceinline__ void store_cols(float* base, int j, const float* f) {
           f32x4{f[8 * o + 4 * h], f[8 * o + 4 * h + 1], f[8 * o + 4 * h + 2], f[8 * o + 4 * h + 3]};
   if constexpr (MP::PAIR)
     *reinterpret_cast<f32x2*>(base + MP::pair_col(j)) = f32x2{f[8 * MP::NO], f[8 * MP::NO + 1]};
+  if constexpr (MP::SINGLE) base[MP::single_col(j)] = f[8 * MP::NO];
 }
 
 // Per-thread column vectors kept in LDS (weights the registers cannot hold):
@@ -154,7 +167,7 @@ __device__ __forceinline__ void store_cols(float* base, int j, const float* f) {
 // plane-major -- plane p holds element group p of every thread, lane j at
 // 16 j bytes -- so a wave's ds_read_b128 covers 1 KB contiguous without bank
 // conflicts (the column-major layout, lanes 32 bytes apart, conflicts 2-way).
-// Planes: octet o half h (4 floats) is plane 2o + h; the pair is last.
+// Planes: octet o half h (4 floats) is plane 2o + h; the pair (or single) is last.
 template <class MP>
 __device__ __forceinline__ void lds_load(const float* base, int j, float* f) {
 #pragma unroll
@@ -170,6 +183,7 @@ __device__ __forceinline__ void lds_load(const float* base, int j, float* f) {
     f[8 * MP::NO] = b[0];
     f[8 * MP::NO + 1] = b[1];
   }
+  if constexpr (MP::SINGLE) f[8 * MP::NO] = base[8 * MP::NO * MP::THREADS + j];
 }
 
 template <class MP>
@@ -182,6 +196,7 @@ __device__ __forceinline__ void lds_store(float* base, int j, const float* f) {
           f32x4{f[8 * o + 4 * h], f[8 * o + 4 * h + 1], f[8 * o + 4 * h + 2], f[8 * o + 4 * h + 3]};
   if constexpr (MP::PAIR)
     reinterpret_cast<f32x2*>(base + 8 * MP::NO * MP::THREADS)[j] = f32x2{f[8 * MP::NO], f[8 * MP::NO + 1]};
+  if constexpr (MP::SINGLE) base[8 * MP::NO * MP::THREADS + j] = f[8 * MP::NO];
 }
 
 // Sum NV (<= 4) values over the NW waves of the workgroup: DPP inside each
@@ -768,11 +783,15 @@ gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restric
 // runs 256 nw threads x 2 columns instead: four times the waves for rows of
 // only 1-2 KB, where one wave per 512 columns leaves the CUs with too few
 // waves to hide the latency of each row step (14% faster at d = 512 and 1024;
-// the forward gains nothing from it).
+// the forward gains nothing from it).  The backward at d = 4608 runs 512
+// threads x 9 columns (an octet and a single column): nine waves of 8 columns
+// would leave a thread 168 VGPRs, which the conv kernel's rings and
+// accumulators do not fit without spilling.
 template <int NW>
 using MapFor = std::conditional_t<NW == 10, ColMap<512, 10>, ColMap<64 * NW, 8>>;
 template <int NW>
-using BwdMapFor = std::conditional_t<NW <= 2, ColMap<256 * NW, 2>, MapFor<NW>>;
+using BwdMapFor =
+    std::conditional_t<NW <= 2, ColMap<256 * NW, 2>, std::conditional_t<NW == 9, ColMap<512, 9>, MapFor<NW>>>;
 
 struct Kernels {
   const void* fwd;
