@@ -42,18 +42,26 @@ def build(verbose: bool = False) -> str:
 
 PROBE_SRC = os.path.join(PKG, "probe", "hbm_probe.hip")
 PROBE_BIN = os.path.join(PKG, "probe", "hbm_probe")
+VALU_SRC = os.path.join(PKG, "probe", "valu_rate.hip")
+VALU_BIN = os.path.join(PKG, "probe", "valu_rate")
 
 
-def build_probe(verbose: bool = False) -> str:
-    """The HBM streaming-ceiling measurement program (not part of libengram)."""
-    tmp = PROBE_BIN + ".tmp"
-    cmd = ["hipcc", *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], "-o", tmp, PROBE_SRC]
+def _build_program(src: str, out: str) -> str:
+    tmp = out + ".tmp"
+    cmd = ["hipcc", *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], "-o", tmp, src]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed ({r.returncode}) building {PROBE_BIN}")
-    os.replace(tmp, PROBE_BIN)
-    return PROBE_BIN
+        raise RuntimeError(f"hipcc failed ({r.returncode}) building {out}")
+    os.replace(tmp, out)
+    return out
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The measurement programs (not part of libengram): the HBM streaming
+    ceilings (hbm_probe) and the VALU issue costs (valu_rate)."""
+    _build_program(VALU_SRC, VALU_BIN)
+    return _build_program(PROBE_SRC, PROBE_BIN)
 
 
 PROBE_LIB_SRC = os.path.join(PKG, "probe", "stream_lib.hip")
