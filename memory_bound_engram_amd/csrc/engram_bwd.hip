@@ -23,8 +23,9 @@
 // A workgroup is 4 token slots x 2 half-row waves (512 threads): wave (u, h)
 // handles slot u's tokens and vectors h + 2i (i = 0..4) of the 640 16-byte
 // vectors of a stream row.  Rows and tokens: up to N = 4096 there are N/64
-// rows of 64 tokens; above that (when 256 divides N) 64 rows of N/64 tokens,
-// so that the 256 workgroups are all resident at once, one per CU.  At step
+// rows of 64 tokens; above that, when 256 divides N, 64 rows of N/64 tokens,
+// so that the 256 workgroups are all resident at once, one per CU (else N/64
+// rows, which then run in two rounds of workgroups).  At step
 // jj the workgroups of all rows together take band jj, the rows * 4
 // consecutive tokens from jj * rows * 4 (slot u of row b: token
 // (jj * 4 + u) * rows + b), so the chip walks the tensors front to back.
@@ -39,7 +40,8 @@
 // of stream s sits in LDS.  Each wave accumulates a x k for its vectors over
 // its tokens in VGPRs; the slots are added in slot order at the end.  The
 // saved row of a slot's next token is fetched a step ahead through the scalar
-// cache, and the next token's loads are issued before this token's stores.
+// cache; the next token's value loads go out as soon as this token's dg sum has
+// read the value, and its other loads before this token's stores.
 // Where delta is 0 -- a masked token (gate 0) or the clamp path -- grad_x = G,
 // grad_key = 0 and there is no grad_weight term, so X, the key and the value
 // are not read; for a masked token grad_value is 0 too and the other streams'
