@@ -447,7 +447,8 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
 // For callers that cannot allocate (code under graph capture, serving loops,
 // harnesses that forbid allocation), the grad_weight partial rows can live in
 // a fixed array of this library instead of the caller's workspace: room for
-// the backward's largest N (8192 tokens = 128 rows of [4][5120] fp32, 10 MiB),
+// N/64 rows at the backward's largest N (128 rows of [4][5120] fp32, 10 MiB;
+// no accepted N uses more, and N = 8192 itself uses 64),
 // held by every GPU the library runs on until the process ends.  In host code
 // `scratch` names a host-side stand-in, never the device memory: its device
 // address is taken once per device with hipGetSymbolAddress (that device

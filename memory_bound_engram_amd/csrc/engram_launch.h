@@ -11,8 +11,9 @@ namespace engram {
 hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
                       float* saved, int64_t n, int grid, hipStream_t stream);
 
-// Enqueue the backward main kernel (4 x N/64 workgroups) and the grad_weight
-// reduction; `partial` holds N/64 rows of [4][5120] fp32 (written, then read
+// Enqueue the backward main kernel (4 workgroups per partial row: N/64 rows,
+// or 64 above N = 4096 when 256 divides N) and the grad_weight reduction;
+// `partial` has room for N/64 rows of [4][5120] fp32 (written, then read
 // back).  With wh/we/gwh/gwe non-null the reduction also writes the
 // product-rule gradients of weight = wh * we.
 hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const float* saved, const void* gout,
