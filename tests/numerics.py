@@ -81,3 +81,22 @@ def check_rel(name, got, ref, rtol, atol=None, max_report=5):
         detail = ", ".join(f"[{i}] got={got[i]!r} ref={ref[i]!r} tol={tol[i]:.3g}" for i in idx)
         raise AssertionError(f"{name}: {int(bad.sum())}/{bad.size} outside tolerance: {detail}")
     return float(np.max(diff / np.maximum(np.abs(ref), 1e-300))) if ref.size else 0.0
+
+
+def subnormal_bf16(bits):
+    """bf16 bits with the exponent cleared (sign and mantissa kept, never zero):
+    subnormal values in [2^-133, 2^-126)."""
+    return ((bits & 0x8000) | ((bits & 0x007F) | 0x0001)).astype(np.uint16)
+
+
+def subnormal_rows_case(n=256, seed=7):
+    """The backward's subnormal case: tokens 0-31 with subnormal grad_out rows,
+    32-63 with subnormal value rows, 64-95 both, the rest normal; mask all ones."""
+    import synth
+    inp = synth.host_inputs(n, seed=seed, p=1.0, grad=True)
+    g, kv = inp["grad_out"], inp["kv"]
+    g[0:32] = subnormal_bf16(g[0:32])
+    kv[32:64, 4 * 5120:] = subnormal_bf16(kv[32:64, 4 * 5120:])
+    g[64:96] = subnormal_bf16(g[64:96])
+    kv[64:96, 4 * 5120:] = subnormal_bf16(kv[64:96, 4 * 5120:])
+    return inp

@@ -51,6 +51,25 @@ def test_bwd_row_partitions_above_4096(gpu, n):
     print(st)
 
 
+def test_bwd_subnormal_rows(gpu):
+    """bf16 subnormal inputs where the backward multiplies them: tokens 0-31
+    have subnormal grad_out rows, tokens 32-63 subnormal value rows, tokens
+    64-95 both; the rest are normal.  The oracle is exact on them, so a flush
+    to zero anywhere in dg or the outputs fails the elementwise bars (a CPU
+    test checks that a planted flush is caught)."""
+    from gpu_util import dev_inputs, f32, run_bwd, to_dev, u16
+    from numerics import subnormal_rows_case
+    from parity import check_bwd
+    import torch
+    inp = subnormal_rows_case()
+    _, saved_ref = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=8)
+    d = dev_inputs(inp, gpu)
+    gx, gkv, gw = run_bwd(d, to_dev(saved_ref, gpu))
+    torch.cuda.synchronize()
+    st = check_bwd(inp, saved_ref, u16(gx), u16(gkv), f32(gw), threads=8)
+    print(st)
+
+
 def test_fwd_bwd_n4096(gpu):
     """N = 4096, mask 0.9, grad_out N(0,1): forward parity, backward parity on
     the oracle's saved, and the device-only chain norm-wise."""
