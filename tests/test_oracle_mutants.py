@@ -111,3 +111,33 @@ def test_pins_reject_mutant(desc, old, new, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_tolerance_scales.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
+
+
+# The mistakes in the method's own arithmetic (forward and backward of the gate
+# and of GateConv), each of which the autograd pins must catch on their own
+# (they run the fp64 entry points; mistakes only in the storage-type path are
+# left to the other pins).
+AUTOGRAD_CAUGHT = [
+    "dx drops the dot term", "dk wrong sign", "dk transposed operand", "dx missing 1/d", "dw uses x^ twice",
+    "dz drops (1 - gate)", "clamp derivative not blocked", "eps outside the sqrt", "rstd without the mean",
+    "sgn(0) taken as +1", "saved rstd fields swapped", "masked token saves the raw gate",
+    "mask ignored in the output", "value gradient reads stream 0 only", "dot over raw (unnormalised) key", "gateconv taps reversed", "gateconv gate without 1/sqrt(d)",
+    "gateconv key normalised with w_v", "gateconv SiLU derivative wrong", "gateconv residual dropped",
+    "gateconv backward conv runs causally", "gateconv rms_v backward sign", "gateconv dv misses alpha",
+    "gateconv dwh drops the key path", "gateconv dcw pairs the wrong token",
+]
+
+
+@pytest.mark.parametrize("desc", AUTOGRAD_CAUGHT)
+def test_autograd_pins_alone_reject_mutant(desc, tmp_path):
+    (old, new), = [(o, n) for dsc, o, n in MUTANTS if dsc == desc]
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(open(SRC).read().replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                           str(lib), str(mutant), "-lm", "-lpthread"])
+    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_autograd_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"autograd pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
