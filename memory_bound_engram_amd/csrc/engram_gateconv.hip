@@ -824,11 +824,17 @@ int gateconv_chunk(int64_t M, int64_t T, int64_t d) {
   // rows per workgroup.  A CU holds about 12 waves of these kernels (their
   // registers), i.e. 12 / (d/512) workgroups; aim at one round of workgroups
   // over the 256 CUs, with at least 32 rows (the halo costs 3 rows a chunk)
-  // and at most 512.  A function of the sizes only, so is the workspace size.
+  // and at most 512.  The narrowest widths (d <= 1024) take chunks down to 16
+  // rows: their rows are too short for a workgroup to hide each row step's
+  // latency, so more workgroups over the same rows pay for the extra halo
+  // (forward 31% faster at d = 512 and 12% at 1024, backward 16% at 512;
+  // down to 8 rows, or 16 at d = 2048 as well, measured slower).  A function
+  // of the sizes only, so is the workspace size.
   const int64_t nw = d / 512;
   const int64_t target = 256 * (nw >= 12 ? 1 : 12 / nw);
   int64_t c = (M * T + target - 1) / target;
-  c = c < 32 ? 32 : c > 512 ? 512 : c;
+  const int64_t lo = nw <= 2 ? 16 : 32;
+  c = c < lo ? lo : c > 512 ? 512 : c;
   return (int)c;
 }
 

@@ -294,10 +294,11 @@ def test_fused_weight_validation():
 def gc_chunk(rows, d):
     nw = d // 512
     target = 256 * (1 if nw >= 12 else 12 // nw)
-    return min(max(-(-rows // target), 32), 512)
+    return min(max(-(-rows // target), 16 if nw <= 2 else 32), 512)
 
 
-@pytest.mark.parametrize("M,T,d", [(1, 1, 512), (2, 37, 5120), (4, 2048, 5120), (8, 4096, 5120), (1, 4194304, 512),
+@pytest.mark.parametrize("M,T,d", [(1, 1, 512), (2, 45, 512), (3, 300, 1024), (2, 37, 5120), (4, 2048, 5120),
+                                   (8, 4096, 5120), (1, 4194304, 512),
                                    (0, 4, 512), (1, 0, 512), (1, 1, 0), (1, 1, 640), (1, 1, 5632), (2, 2097153, 512)])
 def test_gateconv_workspace_formula(M, T, d):
     rows = M * T
