@@ -536,6 +536,100 @@ def bench_same_buffers(torch, synth, eg, dev, stream, placements=3, reps=20, set
         sets.clear()
 
 
+def bench_same_buffers_gateconv(torch, synth, eg, dev, stream, placements=3, reps=20, sets_per_placement=5):
+    """GateConv's kernels against plain streams of exactly their traffic over
+    the same buffers (M = 4 x T = 4096 rows at d = 5120), timed cold as in
+    bench_same_buffers: every call on a different buffer set than the call
+    before it.  The streams (the probe library's, 512-thread workgroups, a row
+    of every tensor per workgroup and step) deal the rows either in chunks of
+    consecutive rows, as GateConv's kernels must for the conv history (256
+    workgroups of 64 rows), or round-robin (lockstep).  One JSON line per
+    placement."""
+    import ctypes
+    plib = ctypes.CDLL(os.path.join(ROOT, "memory_bound_engram_amd", "probe", "libengram_probe.so"))
+    plib.probe_stream.argtypes = [ctypes.c_char_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_void_p]
+    plib.probe_stream.restype = ctypes.c_int
+    M, T, d = GC_M, GC_T, GC_D
+    rows = M * T
+
+    def probe(shape, ins, outs, grid, deal):
+        a_in = (ctypes.c_void_p * len(ins))(*[t.data_ptr() for t in ins])
+        a_out = (ctypes.c_void_p * len(outs))(*[t.data_ptr() for t in outs])
+        rc = plib.probe_stream(shape.encode(), a_in, a_out, rows, grid, deal, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"probe_stream({shape}) returned {rc}")
+
+    def fwd(b):
+        eg.engram_gateconv_fwd(b["H"], b["k"], b["v"], b["wh"], b["wv"], b["cw"], b["Y"], b["vhat"], b["alpha"],
+                               b["rh"], b["rk"], b["rv"], stream=stream)
+
+    def bwd(b):
+        eg.engram_gateconv_bwd(b["dY"], b["H"], b["k"], b["v"], b["wh"], b["wv"], b["cw"], b["vhat"], b["alpha"],
+                               b["rh"], b["rk"], b["rv"], b["dH"], b["dk"], b["dv"], b["dwh"], b["dwv"], b["dcw"],
+                               b["ws"], stream=stream)
+
+    def sfwd(grid, deal):
+        return lambda b: probe("gcfwd", [b["H"], b["k"], b["v"]], [b["Y"], b["vhat"]], grid, deal)
+
+    def sbwd(grid, deal):
+        return lambda b: probe("gcbwd", [b["dY"], b["H"], b["k"], b["v"], b["vhat"]], [b["dH"], b["dk"], b["dv"]],
+                               grid, deal)
+
+    calls = {"gateconv_fwd": fwd, "stream_fwd_chunked256": sfwd(256, 1), "stream_fwd_lockstep256": sfwd(256, 0),
+             "stream_fwd_lockstep1024": sfwd(1024, 0),
+             "gateconv_bwd": bwd, "stream_bwd_chunked256": sbwd(256, 1), "stream_bwd_lockstep256": sbwd(256, 0),
+             "stream_bwd_lockstep1024": sbwd(1024, 0)}
+    own = {"gateconv_fwd": gc_fwd_bytes(M, T, d), "gateconv_bwd": gc_bwd_bytes(M, T, d)}
+    stream_bytes = {"fwd": 5 * 2 * d * rows, "bwd": 8 * 2 * d * rows}
+    for pl in range(placements):
+        torch.cuda.empty_cache()
+        sets = []
+        for _ in range(sets_per_placement):
+            b = {}
+            for name, tid in (("H", synth.ID_GC_H), ("k", synth.ID_GC_K), ("v", synth.ID_GC_V), ("dY", synth.ID_GC_DY)):
+                b[name] = torch.empty((M, T, d), dtype=torch.bfloat16, device=dev)
+                synth.dev_normal_bf16(b[name], SEED, tid)
+            b["wh"] = torch.from_numpy(synth.normal_f32(d, SEED, synth.ID_GC_WH, 1.0, 0.25)).to(dev)
+            b["wv"] = torch.from_numpy(synth.normal_f32(d, SEED, synth.ID_GC_WV, 1.0, 0.25)).to(dev)
+            b["cw"] = torch.from_numpy(synth.normal_f32(4 * d, SEED, synth.ID_GC_CW, 0.0, 0.5).reshape(4, d)).to(dev)
+            for name in ("Y", "vhat", "dH", "dk", "dv"):
+                b[name] = torch.empty((M, T, d), dtype=torch.bfloat16, device=dev)
+            for name in ("alpha", "rh", "rk", "rv"):
+                b[name] = torch.empty((M, T), dtype=torch.float32, device=dev)
+            for name in ("dwh", "dwv"):
+                b[name] = torch.empty(d, dtype=torch.float32, device=dev)
+            b["dcw"] = torch.empty((4, d), dtype=torch.float32, device=dev)
+            b["ws"] = torch.empty(eg.engram_gateconv_bwd_workspace_bytes(M, T, d), dtype=torch.uint8, device=dev)
+            fwd(b)  # the backward reads the forward's saved tensors
+            sets.append(b)
+        R, c = len(sets), 0
+        ev = {k: [] for k in calls}
+        for i in range(2 + reps):
+            for k, f in calls.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                b = sets[c % R]
+                c += 1
+                e0.record(stream)
+                f(b)
+                e1.record(stream)
+                if i >= 2:
+                    ev[k].append((e0, e1))
+        torch.cuda.synchronize()
+        us = {k: round(sorted(a.elapsed_time(z) for a, z in v)[len(v) // 2] * 1e3, 2) for k, v in ev.items()}
+        rate = {k: round((own.get(k) or stream_bytes["fwd" if "fwd" in k else "bwd"]) / (v * 1e-6) / 1e12, 3)
+                for k, v in us.items()}
+        line = {"placement": pl, "rows": rows, "d": d, "buffer_sets": R, "reps": reps, "cold_us": us,
+                "cold_tb_s_own_bytes": rate,
+                "fwd_vs_chunked_stream": round(us["stream_fwd_chunked256"] / us["gateconv_fwd"], 4),
+                "fwd_vs_best_stream": round(min(v for k, v in us.items() if k.startswith("stream_fwd"))
+                                            / us["gateconv_fwd"], 4),
+                "bwd_vs_best_stream": round(min(v for k, v in us.items() if k.startswith("stream_bwd"))
+                                            / us["gateconv_bwd"], 4)}
+        print(json.dumps(line), flush=True)
+        sets.clear()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,6 +654,9 @@ def main():
                     help="instead of the benchmark line, the gate's kernels against plain streams of the "
                          "same traffic over the same buffers (cold, and the backward after the forward), "
                          "for three fresh placements")
+    ap.add_argument("--same-buffers-gateconv", action="store_true",
+                    help="instead of the benchmark line, GateConv's kernels against plain streams of the same "
+                         "traffic over the same buffers, timed cold, for three fresh placements")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device-to-device copy (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -585,6 +682,9 @@ def main():
         del src, dst
     if args.same_buffers:
         bench_same_buffers(torch, synth, eg, dev, torch.cuda.current_stream(dev))
+        return
+    if args.same_buffers_gateconv:
+        bench_same_buffers_gateconv(torch, synth, eg, dev, torch.cuda.current_stream(dev))
         return
     if args.placement:
         bench_placement(torch, synth, eg, dev, torch.cuda.current_stream(dev))

@@ -15,6 +15,8 @@
 //   copy   1 input  (X)                         -> 1 output (X)   50:50
 //   fwd    2 inputs (X, KV)                     -> 1 output (X)   69:31, the forward's mix
 //   bwd    3 inputs (X, KV, G)                  -> 2 outputs (X, KV)  59:41, the backward's mix
+//   gcfwd  3 inputs of 10,240-byte rows          -> 2 outputs      60:40, GateConv's forward
+//   gcbwd  5 inputs of 10,240-byte rows          -> 3 outputs      62.5:37.5, GateConv's backward
 // Token dealing: "lockstep" gives workgroup w the tokens w, w + grid, ... (the
 // workgroups walk the tensors together); "chunked" gives it a contiguous run
 // of tokens; "bands8" cuts the tensors into 8 bands walked in lockstep side

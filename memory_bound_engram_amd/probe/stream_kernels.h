@@ -1,12 +1,13 @@
 // stream_kernels.h -- the plain streaming kernels of the HBM probe.
 //
 // Measurement code, not part of libengram: token-major tensors shaped like
-// the gate's (X-like rows of 2,560 16-byte vectors, KV-like rows of 3,200), a
-// workgroup of THREADS threads per token, non-temporal 16-byte loads of every
-// input row then non-temporal 16-byte stores of every output row (values that
-// depend on the loads, so no load can be dropped).  Used by the probe program
-// (hbm_probe.hip) and by the probe library (stream_lib.hip) that bench.py
-// runs over the gate's own buffers.
+// the gate's (X-like rows of 2,560 16-byte vectors, KV-like rows of 3,200) or
+// GateConv's (rows of 640 at d = 5120), a workgroup of THREADS threads per
+// token, non-temporal 16-byte loads of every input row then non-temporal
+// 16-byte stores of every output row (values that depend on the loads, so no
+// load can be dropped).  Used by the probe program (hbm_probe.hip) and by the
+// probe library (stream_lib.hip) that bench.py runs over the gate's and
+// GateConv's own buffers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,12 +18,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXVecs = 2560;   // 40,960-byte rows
 constexpr int kKvVecs = 3200;  // 51,200-byte rows
+constexpr int kGcVecs = 640;   // 10,240-byte rows (GateConv, d = 5120)
 
 struct Streams {
-  const u32x4* in[3];
-  u32x4* out[2];
-  int in_vecs[3];
-  int out_vecs[2];
+  const u32x4* in[5];
+  u32x4* out[3];
+  int in_vecs[5];
+  int out_vecs[3];
   u32x4* sink;  // written only if an impossible value shows up (keeps read-only loads alive)
 };
 
@@ -139,7 +141,7 @@ __global__ void __launch_bounds__(THREADS) token_stream(Streams s, int64_t ntok,
 struct Shape {
   const char* name;
   int nin, nout;
-  int in_vecs[3], out_vecs[2];
+  int in_vecs[5], out_vecs[3];
 };
 
 static const Shape kShapes[] = {
@@ -148,13 +150,16 @@ static const Shape kShapes[] = {
     {"copy", 1, 1, {kXVecs}, {kXVecs}},
     {"fwd", 2, 1, {kXVecs, kKvVecs}, {kXVecs}},
     {"bwd", 3, 2, {kXVecs, kKvVecs, kXVecs}, {kXVecs, kKvVecs}},
+    // GateConv at d = 5120 (10,240-byte rows): the forward's H, k, v -> Y, vhat
+    // and the backward's dY, H, k, v, vhat -> dH, dk, dv
+    {"gcfwd", 3, 2, {kGcVecs, kGcVecs, kGcVecs}, {kGcVecs, kGcVecs}},
+    {"gcbwd", 5, 3, {kGcVecs, kGcVecs, kGcVecs, kGcVecs, kGcVecs}, {kGcVecs, kGcVecs, kGcVecs}},
 };
 
 typedef void (*KernelFn)(Streams, int64_t, int64_t);
 
-template <int NIN, int NOUT, int THREADS>
+template <int NIN, int NOUT, int THREADS, int MAXV = (kKvVecs + THREADS - 1) / THREADS>
 static KernelFn pick(int deal, bool pipe) {
-  constexpr int MAXV = (kKvVecs + THREADS - 1) / THREADS;
   if (deal == kLockstep) return pipe ? token_stream<NIN, NOUT, THREADS, MAXV, kLockstep, true>
                                      : token_stream<NIN, NOUT, THREADS, MAXV, kLockstep, false>;
   if (deal == kChunked) return pipe ? token_stream<NIN, NOUT, THREADS, MAXV, kChunked, true>
@@ -165,6 +170,9 @@ static KernelFn pick(int deal, bool pipe) {
 
 template <int THREADS>
 static KernelFn kernel_for(const Shape& sh, int deal, bool pipe) {
+  constexpr int GCV = (kGcVecs + THREADS - 1) / THREADS;  // GateConv rows: fewer vectors per thread
+  if (sh.in_vecs[0] == kGcVecs)
+    return sh.nin == 3 ? pick<3, 2, THREADS, GCV>(deal, pipe) : pick<5, 3, THREADS, GCV>(deal, pipe);
   if (sh.nin == 1 && sh.nout == 0) return pick<1, 0, THREADS>(deal, pipe);
   if (sh.nin == 0 && sh.nout == 1) return pick<0, 1, THREADS>(deal, pipe);
   if (sh.nin == 1 && sh.nout == 1) return pick<1, 1, THREADS>(deal, pipe);

@@ -11,6 +11,7 @@ extern "C" {
 // Stream `ntok` tokens of one shape over caller-owned device tensors:
 //   shape "fwd": in = {X [ntok][40960 B], KV [ntok][51200 B]}, out = {[ntok][40960 B]}
 //   shape "bwd": in = {X, KV, G [ntok][40960 B]},             out = {[ntok][40960 B], [ntok][51200 B]}
+//   shapes "gcfwd" / "gcbwd": 3 / 5 inputs and 2 / 3 outputs of [ntok][10240 B]
 // (also "write" and "copy" on X-sized rows; the read-only shape, which has
 // no output to write, is not offered here).  512-thread workgroups,
 // `grid` of them, dealing 0 lockstep / 1 chunked / 2 eight bands (grid a
