@@ -40,12 +40,12 @@ def test_bwd_block_counts(gpu, n):
     _bwd_case(gpu, inp)
 
 
-@pytest.mark.parametrize("n", [4160, 4352, 8128])
+@pytest.mark.parametrize("n", [4160, 4224, 4352, 4608, 6144, 7936, 8128])
 def test_bwd_row_partitions_above_4096(gpu, n):
-    """The backward's other token partitions above N = 4096: 64 rows with an
-    odd step count when 256 divides N (4352 = 64 x 4 x 17), and N/64 rows
-    walked in two rounds of workgroups when it does not (4160: 65 rows; 8128:
-    127 rows, the most the workspace holds)."""
+    """The backward's other token partitions above N = 4096: 64 rows of N/256
+    steps when 256 divides N (4352, 4608, 6144, 7936: 17, 18, 24 and 31 steps),
+    and N/64 rows walked in two rounds of workgroups when it does not (4160,
+    4224: 65 and 66 rows; 8128: 127 rows, the most the workspace holds)."""
     inp = synth.host_inputs(n, seed=n, p=0.7, grad=True)
     st, *_ = _bwd_case(gpu, inp, threads=16)
     print(st)
