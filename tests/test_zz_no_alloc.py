@@ -1,9 +1,11 @@
 """engram_gate_bwd_noalloc (no workspace; the library's own per-GPU partial
 rows) against engram_gate_bwd (caller's workspace), called through the C ABI:
-two calls in a row, the second smaller, each compared bit for bit with the
-workspace backward on the same inputs and saved state, and the second also
-against the oracle.  The second call reuses the array the first one filled,
-so stale partial rows would show."""
+three calls in a row, each compared bit for bit with the workspace backward on
+the same inputs and saved state, and the last also against the oracle.  The
+first, N = 8128, fills 127 of the array's 128 partial rows (the most any
+accepted N uses: 8128 / 64 rows, since 256 does not divide it); the second,
+N = 8192, uses only 64 of them and the third, N = 1088, only 17, so stale
+partial rows left by an earlier call would show."""
 from __future__ import annotations
 
 import numpy as np
@@ -32,7 +34,7 @@ def test_noalloc_backward_matches_workspace_backward(gpu):
     import memory_bound_engram_amd as eg
     from gpu_util import dev_inputs, f32, run_bwd, run_fwd, u16
     from parity import check_bwd
-    for n, seed, p, edge in ((8192, 0, 0.3, True), (1088, 5, 0.9, False)):
+    for n, seed, p, edge in ((8128, 7, 0.5, True), (8192, 0, 0.3, True), (1088, 5, 0.9, False)):
         print(f"noalloc call: N={n} seed={seed} mask p={p} edge rows={edge}", flush=True)
         inp = synth.host_inputs(n, seed=seed, p=p, grad=True, edge=edge)
         d = dev_inputs(inp, gpu)
