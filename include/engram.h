@@ -219,7 +219,8 @@ engram_status engram_gateconv_bwd(const void *dY, const void *H, const void *k, 
                                   int64_t d, void *stream);
 
 /* Scratch bytes of engram_gateconv_bwd (fp32 weight-gradient partials of each
- * token chunk, then one fp32 per row); 0 for sizes the call would reject. */
+ * token chunk, fp32 sums of those partials in blocks of 64 chunks, then one
+ * fp32 per row); 0 for sizes the call would reject. */
 size_t engram_gateconv_bwd_workspace_bytes(int64_t M, int64_t T, int64_t d);
 
 /* Human-readable name of a status code (static storage). */

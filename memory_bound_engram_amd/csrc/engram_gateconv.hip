@@ -731,50 +731,133 @@ gateconv_bwd_hk_kernel(const uint16_t* __restrict__ H, const uint16_t* __restric
 
 // Weight gradients from the [nwg][5][d] partials.  Per column x: s_r = sum
 // over the workgroups of partial row r (64 contiguous chunks of workgroups,
-// each summed sequentially, then the chunk sums in chunk order: fixed for a
-// given nwg), then
+// each summed sequentially, then the chunk sums in the fixed order of
+// ordered_sum_rows), then
 //   drms_w_h = s_0,   dconv_w[i] = w_v s_{1+i},   drms_w_v = sum_i conv_w[i] s_{1+i}.
+// Above 512 workgroups the partials first go through
+// gateconv_reduce_rows_kernel, and this kernel sums its ceil(nwg / 64) rows.
 // The last line is the rms_w_v gradient sum_t du_t u_t / w_v regrouped: with
 // du_t = sum_i conv_w[i] dc_{t+3-i}, both sides add conv_w[i] dc_tau u_t / w_v
 // over the same pairs (t, tau = t + 3 - i) of rows of one sequence.
 constexpr int kRedChunks = 64, kRedGroups = 8;
+constexpr int kRedLanes = kPartRows * kRedGroups;  // (partial row, column group) pairs of a workgroup
+constexpr int kRedRuns = 8, kRedRunLen = kRedChunks / kRedRuns;
+// Above this many partial rows per thread of gateconv_reduce_kernel (above
+// 512 workgroups) the sum runs in two levels.  Each kernel of it costs ~4 us
+// however little it reads, so one level is as fast up to 8 rows per thread
+// (d = 2048 and up at M T = 16384) and two are faster above: d = 512 and 1024
+// have 1024 workgroups and d/32 = 16 or 32 reduce workgroups, which took
+// 12.6 and 13.5 us for the partials alone.
+constexpr int kRedTwoLevelRows = 8;
+
+typedef f32x4 RedRows[kRedChunks][kPartRows][kRedGroups];
+typedef f32x4 RedRuns[kRedRuns][kPartRows][kRedGroups];
+
+// Sum over k of part[k][r][g] for every (r, g), in a fixed order: eight runs
+// of eight consecutive k, each added in k order, then the run sums in run
+// order.  Each run's rows are read into registers before they are added, so
+// a thread has eight LDS reads in flight instead of the compiler's two.  Every
+// thread of the workgroup calls it (it holds a barrier); thread r * 8 + g
+// (< 40) gets the sum of (r, g).
+__device__ __forceinline__ f32x4 ordered_sum_rows(const RedRows& part, RedRuns& runs) {
+  const int tid = threadIdx.x;
+  if (tid < kRedRuns * kRedLanes) {
+    const int h = tid / kRedLanes, r = tid % kRedLanes / kRedGroups, g = tid % kRedGroups;
+    f32x4 v[kRedRunLen];
+#pragma unroll
+    for (int k = 0; k < kRedRunLen; ++k) v[k] = part[h * kRedRunLen + k][r][g];
+    f32x4 t = v[0];
+#pragma unroll
+    for (int k = 1; k < kRedRunLen; ++k) t += v[k];
+    runs[h][r][g] = t;
+  }
+  __syncthreads();
+  f32x4 t = {};
+  if (tid < kRedLanes) {
+    const int r = tid / kRedGroups, g = tid % kRedGroups;
+    f32x4 v[kRedRuns];
+#pragma unroll
+    for (int h = 0; h < kRedRuns; ++h) v[h] = runs[h][r][g];
+    t = v[0];
+#pragma unroll
+    for (int h = 1; h < kRedRuns; ++h) t += v[h];
+  }
+  return t;
+}
 
 __global__ void __launch_bounds__(kRedChunks * kRedGroups)
 gateconv_reduce_kernel(const float* __restrict__ partial, const float* __restrict__ wv, const float* __restrict__ cw,
                        float* __restrict__ dwh, float* __restrict__ dwv, float* __restrict__ dcw, int nwg, int d) {
-  __shared__ f32x4 part[kRedChunks][kPartRows][kRedGroups];
+  __shared__ RedRows part;
+  __shared__ RedRuns runs;
   __shared__ f32x4 tot[kPartRows][kRedGroups];
   const int g = threadIdx.x % kRedGroups, q = threadIdx.x / kRedGroups;
   const int c4 = blockIdx.x * kRedGroups + g;  // float4 column; the grid covers d/4 exactly
   const int ncol4 = d / 4;
   const int b0 = (int)((int64_t)nwg * q / kRedChunks), b1 = (int)((int64_t)nwg * (q + 1) / kRedChunks);
   const f32x4* p4 = reinterpret_cast<const f32x4*>(partial);
+  // the weights of the final step, requested before the sums so that their
+  // latency overlaps them
+  f32x4 w = {}, c[kTaps] = {};
+  if (q == 0) {
+    w = reinterpret_cast<const f32x4*>(wv)[c4];
+#pragma unroll
+    for (int i = 0; i < kTaps; ++i) c[i] = reinterpret_cast<const f32x4*>(cw)[i * ncol4 + c4];
+  }
+  // -0 is the exact identity of IEEE addition (x + -0 = x for every x, +0
+  // and -0 included), so empty chunks and the start of each sum change nothing
   f32x4 s[kPartRows];
 #pragma unroll
-  for (int r = 0; r < kPartRows; ++r) s[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+  for (int r = 0; r < kPartRows; ++r) s[r] = f32x4{-0.f, -0.f, -0.f, -0.f};
+#pragma unroll 8
   for (int b = b0; b < b1; ++b)
 #pragma unroll
     for (int r = 0; r < kPartRows; ++r) s[r] += p4[((int64_t)b * kPartRows + r) * ncol4 + c4];
 #pragma unroll
   for (int r = 0; r < kPartRows; ++r) part[q][r][g] = s[r];
   __syncthreads();
-  if (q < kPartRows) {  // row q of this column group: the chunk sums in chunk order
-    f32x4 t = part[0][q][g];
-    for (int k = 1; k < kRedChunks; ++k) t += part[k][q][g];
-    tot[q][g] = t;
-  }
+  const f32x4 t = ordered_sum_rows(part, runs);  // the chunk sums, in a fixed order
+  if (threadIdx.x < kRedLanes) tot[threadIdx.x / kRedGroups][threadIdx.x % kRedGroups] = t;
   __syncthreads();
   if (q == 0) {
     reinterpret_cast<f32x4*>(dwh)[c4] = tot[0][g];
-    const f32x4 w = reinterpret_cast<const f32x4*>(wv)[c4];
-    f32x4 v = reinterpret_cast<const f32x4*>(cw)[c4] * tot[1][g];
+    f32x4 v = c[0] * tot[1][g];
 #pragma unroll
     for (int i = 0; i < kTaps; ++i) {
       reinterpret_cast<f32x4*>(dcw)[i * ncol4 + c4] = w * tot[1 + i][g];
-      if (i > 0) v += reinterpret_cast<const f32x4*>(cw)[i * ncol4 + c4] * tot[1 + i][g];
+      if (i > 0) v += c[i] * tot[1 + i][g];
     }
     reinterpret_cast<f32x4*>(dwv)[c4] = v;
+  }
+}
+
+// First level of the weight-gradient sum above 512 workgroups: workgroup
+// (x, p) adds the [5][32 columns] blocks of partial rows 64 p ... 64 p + 63
+// (fewer in the last) in the fixed order of ordered_sum_rows and writes them
+// as row p of `sums`
+// ([ceil(nwg / 64)][5][d]).  One thread loads one 16-byte column group of
+// one partial row, so the whole [nwg][5][d] array is read at once by
+// d/32 x ceil(nwg / 64) workgroups; summed by gateconv_reduce_kernel
+// alone, d/32 workgroups (16 at d = 512) read it all and the sum took a
+// fifth of the backward at the narrowest widths.
+__global__ void __launch_bounds__(kRedChunks * kRedGroups)
+gateconv_reduce_rows_kernel(const float* __restrict__ partial, float* __restrict__ sums, int nwg, int d) {
+  __shared__ RedRows part;
+  __shared__ RedRuns runs;
+  const int g = threadIdx.x % kRedGroups, q = threadIdx.x / kRedGroups;
+  const int ncol4 = d / 4;
+  const int b0 = blockIdx.y * kRedChunks;
+  const int nb = nwg - b0 < kRedChunks ? nwg - b0 : kRedChunks;  // rows of this block, >= 1
+  const f32x4* p4 = reinterpret_cast<const f32x4*>(partial);
+#pragma unroll
+  for (int r = 0; r < kPartRows; ++r)  // rows past the last are -0, the exact identity of addition
+    part[q][r][g] = q < nb ? p4[((int64_t)(b0 + q) * kPartRows + r) * ncol4 + blockIdx.x * kRedGroups + g]
+                           : f32x4{-0.f, -0.f, -0.f, -0.f};
+  __syncthreads();
+  const f32x4 t = ordered_sum_rows(part, runs);
+  if (threadIdx.x < kRedLanes) {  // (partial row r, column group h) of this workgroup
+    const int r = threadIdx.x / kRedGroups, h = threadIdx.x % kRedGroups;
+    reinterpret_cast<f32x4*>(sums)[((int64_t)blockIdx.y * kPartRows + r) * ncol4 + blockIdx.x * kRedGroups + h] = t;
   }
 }
 
@@ -821,17 +904,21 @@ const Kernels* kernels_for_width(int64_t d) {
 }  // namespace
 
 int gateconv_chunk(int64_t M, int64_t T, int64_t d) {
-  // rows per workgroup.  A CU holds about 12 waves of these kernels (their
-  // registers), i.e. 12 / (d/512) workgroups; aim at one round of workgroups
-  // over the 256 CUs, with at least 32 rows (the halo costs 3 rows a chunk)
-  // and at most 512.  The narrowest widths (d <= 1024) take chunks down to 16
-  // rows: their rows are too short for a workgroup to hide each row step's
-  // latency, so more workgroups over the same rows pay for the extra halo
+  // rows per workgroup.  A CU holds 8 waves of the backward's conv kernel
+  // (182-229 VGPRs: two waves per SIMD), i.e. 8 / (d/512) workgroups of d/512
+  // waves (at least one); aim at one round of workgroups over the 256 CUs,
+  // with at least 32 rows (the halo costs 3 rows a chunk) and at most 512.
+  // (Counting 12 waves a CU put d = 2560 and 3072 into two rounds of 32-row
+  // chunks, one workgroup per CU at a time: their backward ran at 3.6-4.0
+  // TB/s against 4.5 for d = 3584.)  The narrowest widths (d <= 1024) take
+  // chunks down to 16 rows: their rows are too short for a workgroup to hide
+  // each row step's latency, so more workgroups over the same rows pay for
+  // the extra halo
   // (forward 31% faster at d = 512 and 12% at 1024, backward 16% at 512;
   // down to 8 rows, or 16 at d = 2048 as well, measured slower).  A function
   // of the sizes only, so is the workspace size.
   const int64_t nw = d / 512;
-  const int64_t target = 256 * (nw >= 12 ? 1 : 12 / nw);
+  const int64_t target = 256 * (nw >= 8 ? 1 : 8 / nw);
   int64_t c = (M * T + target - 1) / target;
   const int64_t lo = nw <= 2 ? 16 : 32;
   c = c < lo ? lo : c > 512 ? 512 : c;
@@ -840,9 +927,14 @@ int gateconv_chunk(int64_t M, int64_t T, int64_t d) {
 
 int64_t gateconv_workgroups(int64_t M, int64_t T, int chunk) { return (M * T + chunk - 1) / chunk; }
 
+// Rows of the first-level sums of the weight-gradient partials.
+static int64_t gateconv_sum_rows(int64_t nwg) { return (nwg + kRedChunks - 1) / kRedChunks; }
+
 size_t gateconv_bwd_workspace(int64_t M, int64_t T, int64_t d, int chunk) {
-  // [nwg][5][d] fp32 weight-gradient partials, then the per-row ds [M*T]
-  return (size_t)gateconv_workgroups(M, T, chunk) * kPartRows * (size_t)d * sizeof(float) +
+  // [nwg][5][d] fp32 weight-gradient partials, [ceil(nwg / 64)][5][d] fp32
+  // first-level sums of them, then the per-row ds [M*T]
+  const int64_t nwg = gateconv_workgroups(M, T, chunk);
+  return (size_t)(nwg + gateconv_sum_rows(nwg)) * kPartRows * (size_t)d * sizeof(float) +
          (size_t)(M * T) * sizeof(float);
 }
 
@@ -872,8 +964,10 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
                  *vhp = static_cast<const uint16_t*>(vhat);
   uint16_t *dhp = static_cast<uint16_t*>(dH), *dkp = static_cast<uint16_t*>(dK), *dvp = static_cast<uint16_t*>(dV);
   const int64_t nwg = gateconv_workgroups(M, T, chunk);
+  const int64_t nsum = gateconv_sum_rows(nwg);
   float* partial = static_cast<float*>(workspace);
-  float* ds = partial + nwg * kPartRows * d;
+  float* sums = partial + nwg * kPartRows * d;
+  float* ds = sums + nsum * kPartRows * d;
   int rows = (int)(M * T), Ti = (int)T, di = (int)d, ch = chunk;
   void* a1[] = {&gp, &vp, &wv, &cw, &vhp, &alpha, &rrv, &dvp, &ds, &partial, &rows, &Ti, &ch};
   hipError_t e = hipLaunchKernel(kn->conv, dim3((unsigned)nwg), dim3((unsigned)kn->bwd_threads), a1, 0, stream);
@@ -884,6 +978,15 @@ hipError_t launch_gateconv_bwd(const void* dY, const void* H, const void* K, con
   if (e != hipSuccess) return e;
   const float* cp = partial;
   int nwi = (int)nwg;
+  if (nwg > kRedChunks * kRedTwoLevelRows) {  // first level: blocks of 64 partial rows -> nsum rows
+    void* a4[] = {&cp, &sums, &nwi, &di};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_rows_kernel),
+                        dim3((unsigned)(d / 4 / kRedGroups), (unsigned)nsum), dim3(kRedChunks * kRedGroups), a4, 0,
+                        stream);
+    if (e != hipSuccess) return e;
+    cp = sums;
+    nwi = (int)nsum;
+  }
   void* a3[] = {&cp, &wv, &cw, &dwh, &dwv, &dcw, &nwi, &di};
   return hipLaunchKernel(reinterpret_cast<const void*>(&gateconv_reduce_kernel), dim3((unsigned)(d / 4 / kRedGroups)),
                          dim3(kRedChunks * kRedGroups), a3, 0, stream);

@@ -33,7 +33,8 @@ hipError_t scratch_partials(float** out);
 hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hipStream_t stream);
 
 // GateConv: rows per workgroup chunk (a function of M*T and d only), the number of
-// workgroups, and the launchers (forward; backward main + weight-gradient reduce).
+// workgroups, and the launchers (forward; backward main + weight-gradient
+// reduce, in two levels above 512 workgroups).
 int gateconv_chunk(int64_t M, int64_t T, int64_t d);
 int64_t gateconv_workgroups(int64_t M, int64_t T, int chunk);
 size_t gateconv_bwd_workspace(int64_t M, int64_t T, int64_t d, int chunk);

@@ -151,9 +151,11 @@ def oracle_bwd(inp, saved):
 # M, T, d: several chunks with a ragged last one and chunks that cross sequence
 # boundaries (at d = 512 also with 16-row chunks); sequences shorter than the
 # conv window; a single row; every supported width, 512 to 5120 in steps of
-# 512 (each has its own kernels; 4608 runs 9 columns a thread).
+# 512 (each has its own kernels; 4608 runs 9 columns a thread); and more than
+# 512 workgroups (563 at d = 512, 625 at d = 2048), where the weight gradients
+# are summed in two levels and the last block of 64 partial rows is ragged.
 SHAPES = [(2, 37, 5120), (3, 5, 1024), (1, 1, 512), (5, 300, 2048), (7, 3, 3072), (1, 2, 4096), (2, 700, 1536),
-          (2, 70, 4608), (3, 33, 2560), (1, 129, 3584), (2, 45, 512)]
+          (2, 70, 4608), (3, 33, 2560), (1, 129, 3584), (2, 45, 512), (3, 3000, 512), (1, 20000, 2048)]
 
 
 @pytest.mark.parametrize("M,T,d", SHAPES)
