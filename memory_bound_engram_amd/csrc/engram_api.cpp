@@ -176,7 +176,7 @@ static bool gateconv_dims_ok(int64_t M, int64_t T, int64_t d) {
 
 size_t engram_gateconv_bwd_workspace_bytes(int64_t M, int64_t T, int64_t d) {
   if (!gateconv_dims_ok(M, T, d)) return 0;
-  return engram::gateconv_bwd_workspace(M, T, d, engram::gateconv_chunk(M, T, d));
+  return engram::gateconv_bwd_workspace(M, T, d, engram::gateconv_chunk(M, T, d, true));
 }
 
 engram_status engram_gateconv_fwd(const void* H, const void* k, const void* v, const float* rms_w_h,
@@ -196,7 +196,7 @@ engram_status engram_gateconv_fwd(const void* H, const void* k, const void* v, c
                         range_of(rrms_h, sb), range_of(rrms_k, sb), range_of(rrms_v, sb)};
   if (any_overlap(in, 6, outs, 6)) return ENGRAM_ERR_OVERLAP;
   return launched(engram::launch_gateconv_fwd(H, k, v, rms_w_h, rms_w_v, conv_w, Y, vhat, alpha, rrms_h, rrms_k,
-                                              rrms_v, M, T, d, eps, engram::gateconv_chunk(M, T, d),
+                                              rrms_v, M, T, d, eps, engram::gateconv_chunk(M, T, d, false),
                                               (hipStream_t)stream));
 }
 
@@ -224,7 +224,7 @@ engram_status engram_gateconv_bwd(const void* dY, const void* H, const void* k, 
   if (any_overlap(in, 12, outs, 7)) return ENGRAM_ERR_OVERLAP;
   return launched(engram::launch_gateconv_bwd(dY, H, k, v, rms_w_h, rms_w_v, conv_w, vhat, alpha, rrms_h, rrms_k,
                                               rrms_v, dH, dk, dv, drms_w_h, drms_w_v, dconv_w, workspace, M, T, d,
-                                              engram::gateconv_chunk(M, T, d), (hipStream_t)stream));
+                                              engram::gateconv_chunk(M, T, d, true), (hipStream_t)stream));
 }
 
 const char* engram_status_string(int status) {

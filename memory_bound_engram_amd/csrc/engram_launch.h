@@ -35,7 +35,7 @@ hipError_t launch_fused_weight(const void* wh, const void* we, float* weight, hi
 // GateConv: rows per workgroup chunk (a function of M*T and d only), the number of
 // workgroups, and the launchers (forward; backward main + weight-gradient
 // reduce, in two levels above 512 workgroups).
-int gateconv_chunk(int64_t M, int64_t T, int64_t d);
+int gateconv_chunk(int64_t M, int64_t T, int64_t d, bool bwd);
 int64_t gateconv_workgroups(int64_t M, int64_t T, int chunk);
 size_t gateconv_bwd_workspace(int64_t M, int64_t T, int64_t d, int chunk);
 hipError_t launch_gateconv_fwd(const void* H, const void* K, const void* V, const float* wh, const float* wv,

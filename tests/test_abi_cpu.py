@@ -292,8 +292,10 @@ def test_fused_weight_validation():
 # ---------------- GateConv ----------------
 
 def gc_chunk(rows, d):
+    """Rows per workgroup chunk of the backward (which sizes its workspace)."""
     nw = d // 512
-    target = 256 * (1 if nw >= 8 else 8 // nw)
+    waves = 4 if nw == 5 else nw  # d = 2560 runs the backward 256 threads x 10 columns
+    target = 256 * (1 if waves >= 8 else 8 // waves)
     return min(max(-(-rows // target), 16 if nw <= 2 else 32), 512)
 
 
