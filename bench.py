@@ -82,10 +82,39 @@ KERNEL_SOURCES = {  # what decides each recorded kernel's traffic: its code and 
 }
 
 
+def code_only(src):
+    """C++ source without its comments, runs of whitespace collapsed: a comment
+    edit leaves it (and the recorded traffic keyed on it) unchanged, a code
+    edit does not.  String and character literals are kept whole."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(kernel):
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", name), "rb").read())
+        with open(os.path.join(ROOT, "memory_bound_engram_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

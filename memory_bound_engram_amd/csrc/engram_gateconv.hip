@@ -26,10 +26,11 @@
 // below): d = 5120 runs 512 threads x 10 columns (an octet and a pair), so
 // the workgroup is a power of two and each thread has 256 VGPRs; other widths
 // run d/8 threads x 8 columns (one octet), except the backward at d = 512 and
-// 1024, which runs d/2 threads x 2 columns (one pair).  Row sums reduce with DPP inside
-// each wave and across waves through LDS, in a fixed order.  Weight gradients
-// are per-workgroup fp32 partials in the workspace, summed by a last kernel
-// in a fixed order.
+// 1024 (d/2 threads x 2 columns, one pair), at d = 2560 (256 threads x 10
+// columns) and at d = 4608 (512 threads x 9 columns).  Row sums reduce with
+// DPP inside each wave and across waves through LDS, in a fixed order.
+// Weight gradients are per-workgroup fp32 partials in the workspace, summed
+// by one last kernel (two above 512 workgroups) in a fixed order.
 #include "engram_device.h"
 #include "engram_launch.h"
 

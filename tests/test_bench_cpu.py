@@ -76,10 +76,21 @@ def test_recorded_traffic_invalidated_by_a_source_change(tmp_path):
     with open(root / "profiles" / "traffic.json", "w") as f:
         json.dump(rec, f)
     assert b.recorded_traffic("bwd") == rec["bwd"]["bytes_per_launch"]
-    with open(root / "memory_bound_engram_amd" / "csrc" / "engram_bwd.hip", "a") as f:
-        f.write("\n// edited\n")
+    bwd_src = root / "memory_bound_engram_amd" / "csrc" / "engram_bwd.hip"
+    with open(bwd_src, "a") as f:  # comments and layout are not code: the record stands
+        f.write("\n// a comment\n/* another\n   one */   \n")
+    assert b.recorded_traffic("bwd") == rec["bwd"]["bytes_per_launch"]
+    with open(bwd_src, "a") as f:  # a code edit voids it
+        f.write("static const int engram_edited = 1;\n")
     assert b.recorded_traffic("bwd") is None
     assert b.recorded_traffic("fwd") == rec["fwd"]["bytes_per_launch"]  # other kernels keep their record
+
+
+def test_code_only_strips_comments_not_literals():
+    b = load_bench()
+    src = 'int a = 1;  // one\n/* two\n */ const char* s = "x // y /* z */";\nchar q = \'\\\'\';\n'
+    assert b.code_only(src) == 'int a = 1; const char* s = "x // y /* z */"; char q = \'\\\'\';'
+    assert b.code_only("a/b") == "a/b" and b.code_only("a /*x*/b") == "a b"
 
 
 def test_more_than_one_gpu_is_refused():
