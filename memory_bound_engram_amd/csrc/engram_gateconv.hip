@@ -25,9 +25,9 @@
 // intermediates.  Each thread covers C columns of a row (the column map
 // below): d = 5120 runs 512 threads x 10 columns (an octet and a pair), so
 // the workgroup is a power of two and each thread has 256 VGPRs; other widths
-// run d/8 threads x 8 columns (one octet), except the backward at d = 512 and
-// 1024 (d/2 threads x 2 columns, one pair), at d = 2560 (256 threads x 10
-// columns) and at d = 4608 (512 threads x 9 columns).  Row sums reduce with
+// run d/8 threads x 8 columns (one octet), except the backward at d = 512,
+// 1024 and 1536 (d/2 threads x 2 columns, one pair), at d = 2560 (256
+// threads x 10 columns) and at d = 4608 (512 threads x 9 columns).  Row sums reduce with
 // DPP inside each wave and across waves through LDS, in a fixed order.
 // Weight gradients are per-workgroup fp32 partials in the workspace, summed
 // by one last kernel (two above 512 workgroups) in a fixed order.
@@ -40,7 +40,8 @@ namespace engram {
 namespace {
 
 constexpr int kTaps = 4;
-constexpr int kMaxWaves = 10;
+constexpr int kMaxWaves = 16;   // waves of a workgroup (the cross-wave sum adds 16 lanes)
+constexpr int kMaxWidths = 10;  // widths d = 512 ... 5120
 constexpr int kPartRows = 1 + kTaps;  // weight-gradient partial rows per workgroup: rms_w_h, conv_w taps
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,7 +64,7 @@ struct ColMap {
   static constexpr bool SINGLE = (C_ % 8) == 1;
   static constexpr int NW = THREADS_ / 64;
   static_assert(C_ % 8 == 0 || C_ % 8 == 2 || C_ % 8 == 1, "columns per thread: octets and at most one pair or single");
-  static_assert(THREADS_ % 64 == 0 && NW >= 1 && NW <= kMaxWaves, "whole waves, at most ten");
+  static_assert(THREADS_ % 64 == 0 && NW >= 1 && NW <= kMaxWaves, "whole waves, at most sixteen");
   __device__ static constexpr int oct_col(int j, int o) { return 8 * j + 8 * THREADS_ * o; }
   __device__ static constexpr int pair_col(int j) { return 8 * THREADS_ * NO + 2 * j; }
   __device__ static constexpr int single_col(int j) { return 8 * THREADS_ * NO + j; }
@@ -429,9 +430,10 @@ gateconv_bwd_conv_kernel(const uint16_t* __restrict__ dY, const uint16_t* __rest
                          float* __restrict__ partial, int rows, int T, int chunk) {
   constexpr int d = MP::d, C = MP::C;
   // conv_w gradient taps kRegTaps..3 accumulate in LDS when more than eight
-  // waves leave a thread at most 168 VGPRs (d = 4608: taps 2 and 3, the split
-  // with the least spilling, 16 bytes a lane); all four stay in registers otherwise
-  constexpr int kRegTaps = MP::NW > 8 ? 2 : kTaps;
+  // waves of octet columns leave a thread at most 168 VGPRs (taps 2 and 3, the
+  // split with the least spilling; no current map needs it since d = 4608
+  // runs 512 x 9); all four stay in registers otherwise
+  constexpr int kRegTaps = MP::NW > 8 && MP::C >= 8 ? 2 : kTaps;
   constexpr int kLdsTapPlanes = kTaps - kRegTaps;
   // the combined tap weights W_i = conv_w[i] w_v [4][d] (, taps 2-3 grads [2][d]):
   // c = sum_i W_i (u / w_v)_{t-3+i} and w_v du_t = sum_i W_i dc_{t+3-i} both use them
@@ -863,9 +865,9 @@ gateconv_reduce_rows_kernel(const float* __restrict__ partial, float* __restrict
 }
 
 // The column map for width d = 512 nw: 512 threads x 10 columns for d = 5120,
-// else 64 nw threads x 8 columns.  The backward of the two narrowest widths
+// else 64 nw threads x 8 columns.  The backward of the three narrowest widths
 // runs 256 nw threads x 2 columns instead: four times the waves for rows of
-// only 1-2 KB, where one wave per 512 columns leaves the CUs with too few
+// only 1-3 KB, where one wave per 512 columns leaves the CUs with too few
 // waves to hide the latency of each row step (14% faster at d = 512 and 1024;
 // the forward gains nothing from it).  The backward at d = 4608 runs 512
 // threads x 9 columns (an octet and a single column): nine waves of 8 columns
@@ -879,7 +881,7 @@ template <int NW>
 using MapFor = std::conditional_t<NW == 10, ColMap<512, 10>, ColMap<64 * NW, 8>>;
 template <int NW>
 using BwdMapFor = std::conditional_t<
-    NW <= 2, ColMap<256 * NW, 2>,
+    NW <= 3, ColMap<256 * NW, 2>,
     std::conditional_t<NW == 9, ColMap<512, 9>, std::conditional_t<NW == 5, ColMap<256, 10>, MapFor<NW>>>>;
 
 struct Kernels {
@@ -899,11 +901,11 @@ Kernels kernels_for() {
 }
 
 const Kernels* kernels_for_width(int64_t d) {
-  static const Kernels table[kMaxWaves] = {kernels_for<1>(), kernels_for<2>(), kernels_for<3>(), kernels_for<4>(),
+  static const Kernels table[kMaxWidths] = {kernels_for<1>(), kernels_for<2>(), kernels_for<3>(), kernels_for<4>(),
                                            kernels_for<5>(), kernels_for<6>(), kernels_for<7>(), kernels_for<8>(),
                                            kernels_for<9>(), kernels_for<10>()};
   const int64_t nw = d / 512;
-  if (d % 512 != 0 || nw < 1 || nw > kMaxWaves) return nullptr;
+  if (d % 512 != 0 || nw < 1 || nw > kMaxWidths) return nullptr;
   return &table[nw - 1];
 }
 
@@ -924,7 +926,9 @@ int gateconv_chunk(int64_t M, int64_t T, int64_t d, bool bwd) {
   // down to 8 rows, or 16 at d = 2048 as well, measured slower).  A function
   // of the sizes only, so is the workspace size.
   const int64_t nw = d / 512;
-  const int64_t waves = bwd && nw == 5 ? 4 : nw;  // the backward's 256 x 10 map at d = 2560
+  // the backward's maps at d = 1536 (768 x 2: 12 waves of ~64 VGPRs, two
+  // workgroups a CU) and d = 2560 (256 x 10: 4 waves, two a CU) count as 4
+  const int64_t waves = bwd && (nw == 3 || nw == 5) ? 4 : nw;
   const int64_t target = 256 * (waves >= 8 ? 1 : 8 / waves);
   int64_t c = (M * T + target - 1) / target;
   const int64_t lo = nw <= 2 ? 16 : 32;

@@ -294,13 +294,14 @@ def test_fused_weight_validation():
 def gc_chunk(rows, d):
     """Rows per workgroup chunk of the backward (which sizes its workspace)."""
     nw = d // 512
-    waves = 4 if nw == 5 else nw  # d = 2560 runs the backward 256 threads x 10 columns
+    waves = 4 if nw in (3, 5) else nw  # d = 1536 and 2560 run the backward on 768 x 2 and 256 x 10 maps
     target = 256 * (1 if waves >= 8 else 8 // waves)
     return min(max(-(-rows // target), 16 if nw <= 2 else 32), 512)
 
 
 @pytest.mark.parametrize("M,T,d", [(1, 1, 512), (2, 45, 512), (3, 300, 1024), (2, 37, 5120), (4, 2048, 5120),
-                                   (8, 4096, 5120), (1, 4194304, 512),
+                                   (8, 4096, 5120), (1, 4194304, 512), (4, 4096, 1536), (4, 4096, 2560),
+                                   (1, 100000, 1536), (3, 33, 2560),
                                    (0, 4, 512), (1, 0, 512), (1, 1, 0), (1, 1, 640), (1, 1, 5632), (2, 2097153, 512)])
 def test_gateconv_workspace_formula(M, T, d):
     rows = M * T
