@@ -8,8 +8,8 @@
 //   out = mask ? bf16(x + gate v) : x (bit copy), saved = (mask?gate:0, dot, rstd_X, rstd_key).
 //
 // Mapping: one wave64 per (token, stream).  A workgroup is 4 waves -- the 4
-// streams of one token -- and the grid is persistent (one workgroup per CU,
-// striding over tokens).  Lane l of wave s covers vectors l + 64 i
+// streams of one token -- and strides over the tokens by the grid size (the
+// launcher's grid holds a few workgroups per CU; one is resident at a time).  Lane l of wave s covers vectors l + 64 i
 // (i = 0..9, 8 bf16 each) of stream s's rows, so every wave instruction
 // moves 1 KB of contiguous memory and the three per-row sums (x.x, k.k,
 // x.w.k) reduce inside the wave with DPP: no LDS and no barrier.  The weight

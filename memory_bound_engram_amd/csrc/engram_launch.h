@@ -6,7 +6,7 @@
 
 namespace engram {
 
-// Enqueue the forward kernel with `grid` persistent workgroups (no saved
+// Enqueue the forward kernel with `grid` workgroups striding over the tokens (no saved
 // state is written when saved == nullptr).
 hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
                       float* saved, int64_t n, int grid, hipStream_t stream);
