@@ -213,14 +213,17 @@ def test_gateconv_bwd_deterministic(gpu):
         assert np.array_equal(a[x].view(np.uint8), b[x].view(np.uint8)), x
 
 
-def test_gateconv_full_size(gpu):
-    """The benchmarked workload, M=4 sequences of T=4096 tokens, d=5120, in the
-    launch configuration the benchmark times: every output against the oracle."""
-    M, T, d = 4, 4096, 5120
+@pytest.mark.parametrize("d", [5120, 2560, 1536])
+def test_gateconv_full_size(gpu, d):
+    """M=4 sequences of T=4096 tokens, every output against the oracle: at
+    d=5120 the benchmarked workload in the launch configuration the benchmark
+    times; at d=2560 and 1536 the backward's 256 x 10 and 768 x 2 column maps
+    over 512 workgroups, two resident per CU."""
+    M, T = 4, 4096
     inp = synth.gateconv_inputs(M, T, d, seed=2024)
     ref = oracle_fwd(inp)
     st = check_fwd(inp, run_fwd(inp, gpu), ref)
-    print(f"gateconv fwd full size: Y bit-equal to rounded oracle {st['bit_equal_to_rounded_oracle']}/{st['n']}")
+    print(f"gateconv fwd full size d={d}: Y bit-equal to rounded oracle {st['bit_equal_to_rounded_oracle']}/{st['n']}")
     saved = rounded_saved(ref)
     del ref
     check_bwd(run_bwd(inp, saved, gpu), oracle_bwd(inp, saved))
