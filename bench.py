@@ -16,8 +16,11 @@ The step's inputs are those of the N = 8192 forward workload (configuration
 1: mask 0.9, no edge rows), run through forward and backward at the
 backward's maximum N, the size of configuration 4.
 
-Also reported: forward-only and backward-only rates at N = 8192 (from HIP
-events around each call inside the timed region); a `configs` object with
+The step rate (value, ms_per_step) is K steps back to back with nothing else
+on the stream.  Also reported: forward-only and backward-only rates at
+N = 8192, from HIP events around each call in a second pass of the same K
+steps (each recorded event holds the stream for a few microseconds between
+calls, so the events stay out of the rate's pass); a `configs` object with
 the GPU time, tokens/s and fraction of 8 TB/s of each of the five workload
 configurations (0: forward N = 64; 1: forward N = 8192; 2: forward +
 backward N = 4096; 3: forward N = 1,048,512 in one launch; 4: forward +
@@ -746,9 +749,22 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # the step rate: K steps back to back with nothing else on the stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(K):
+        b = sets[i % R]
+        fwd(b)
+        bwd(b)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # per-call durations: a second pass of the same K steps with HIP events
+    # around each call on the launch stream.  Each recorded event holds the
+    # stream for a few microseconds between calls (about 10 us a step here),
+    # so the events stay out of the pass that gives the rate.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     for i in range(K):
         b = sets[i % R]
         ev[i][0].record(stream)
@@ -757,13 +773,14 @@ def main():
         bwd(b)
         ev[i][2].record(stream)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_with_events = time.perf_counter() - t1
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
 
     fwd_gbps = fwd_bytes(n) / (fwd_ms * 1e-3) / 1e9
     bwd_gbps = bwd_bytes(n) / (bwd_ms * 1e-3) / 1e9
     both_gbps = (fwd_bytes(n) + bwd_bytes(n)) / ((fwd_ms + bwd_ms) * 1e-3) / 1e9
+    step_gbps = (fwd_bytes(n) + bwd_bytes(n)) / (elapsed / K) / 1e9
     dominant = "bwd" if bwd_ms >= fwd_ms else "fwd"
     if dominant == "bwd":
         roof = {"kernel": "engram_gate_bwd (main kernel + grad_weight column reduce)",
@@ -803,6 +820,11 @@ def main():
                 "tensor_gbps": round(bwd_gbps, 1), "frac_of_peak": round(bwd_gbps / PEAK_GBPS, 4)},
         "fwd_bwd": {"tokens_per_s": round(n / ((fwd_ms + bwd_ms) * 1e-3), 1),
                     "tensor_gbps": round(both_gbps, 1), "frac_of_peak": round(both_gbps / PEAK_GBPS, 4)},
+        "step": {"us": round(elapsed / K * 1e6, 2), "tensor_gbps": round(step_gbps, 1),
+                 "frac_of_peak": round(step_gbps / PEAK_GBPS, 4),
+                 "us_with_per_call_events": round(elapsed_with_events / K * 1e6, 2),
+                 "timing": "value and ms_per_step: K steps back to back, no per-call events; fwd, bwd, "
+                           "fwd_bwd and roofline: a second pass of the K steps with HIP events around each call"},
         "roofline": roof,
     }
     sets.clear()
