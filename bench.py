@@ -322,12 +322,15 @@ def oracle_rate(op, n, p, edge, seconds=3.0, sample=2048):
 
 
 def measure_config(torch, synth, eg, dev, stream, c, rotate):
-    """One workload configuration on the GPU: time per call from HIP events on
-    the launch stream, tokens/s, tensor-byte GB/s and its fraction of 8 TB/s.
-    Configurations 0-2 cycle `rotate` independent buffer sets (so no call
-    finds its inputs in the 256 MB cache); configuration 3 has one set
-    (140 GB) and reports the median of its launches; configuration 4 repeats
-    its 1000 launches on one set, back to back on one stream, as specified."""
+    """One workload configuration on the GPU: time per call (the configuration's
+    launches back to back on the launch stream, between two HIP events, over
+    their count), tokens/s, tensor-byte GB/s and its fraction of 8 TB/s; below
+    1000 launches also the median of single calls, each between two events of
+    its own (each recorded event holds the stream a few microseconds, which
+    the back-to-back time leaves out).  Configurations 0-2 cycle `rotate`
+    independent buffer sets (so no call finds its inputs in the 256 MB cache);
+    configuration 3 has one set (140 GB); configuration 4 repeats its 1000
+    launches on one set, as specified."""
     n, op = c["tokens"], c["op"]
     grad = op != "fwd"
     R = rotate if c["config"] <= 2 else 1
@@ -372,30 +375,34 @@ def measure_config(torch, synth, eg, dev, stream, c, rotate):
         call(sets[i % R])
     torch.cuda.synchronize()
     K = c["launches"]
-    if K >= 1000:  # one stream, back to back: the loop's time over its launches
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(K):
-            call(sets[i % R])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / K
-    else:  # median of per-call times
+    # the calls back to back on one stream: the time of the K calls over K
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(K):
+        call(sets[i % R])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    us_median = None
+    if K < 1000:  # also the median of single calls, each between two events of its own
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-        for i, (e0, e1) in enumerate(ev):
-            e0.record(stream)
+        for i, (a, z) in enumerate(ev):
+            a.record(stream)
             call(sets[i % R])
-            e1.record(stream)
+            z.record(stream)
         torch.cuda.synchronize()
-        us = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[K // 2] * 1e3
+        us_median = sorted(a.elapsed_time(z) for a, z in ev)[K // 2] * 1e3
     byt = fwd_bytes(n) + (bwd_bytes(n) if grad else 0)
     gbps = byt / (us * 1e-6) / 1e9
     sets.clear()
     torch.cuda.empty_cache()
     line = {"config": c["config"], "workload": c["desc"], "op": op, "tokens": n, "mask_p": c["mask_p"],
             "edge_rows": c["edge"], "launches": K, "buffer_sets_rotated": R, "us_per_call": round(us, 2),
+            "us_per_call_timing": "K calls back to back on one stream, over K",
             "tokens_per_s": round(n / (us * 1e-6), 1), "tensor_bytes_per_call": byt,
             "tensor_gbps": round(gbps, 1), "frac_of_peak_tensor_bytes": round(gbps / PEAK_GBPS, 4)}
+    if us_median is not None:
+        line["us_median_single_call"] = round(us_median, 2)
     moved = recorded_config_traffic(c["config"])
     if moved:
         # the HBM bytes a call actually moves (the backward skips reads where delta is 0)
