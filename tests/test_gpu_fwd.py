@@ -52,6 +52,33 @@ def test_fwd_edge_rows(gpu):
         assert saved[t, s, 0] == (0.5 if inp["mask"][t] else 0.0)
 
 
+def test_fwd_subnormal_rows(gpu):
+    """bf16 subnormal inputs where the forward adds or scales them, mask all
+    ones: tokens 0-31 have subnormal X rows and a zero value row, so out must
+    be X bit for bit (out = x + gate * 0); tokens 32-63 have zero X rows and a
+    subnormal value row, so dot = 0, gate = 1/2 and out = bf16(v / 2).  A
+    flush to zero of a subnormal operand or result in the forward breaks the
+    one-ulp bar on out; both sides take the dot of the subnormal X rows far
+    inside the clamp (rstd_X = eps^-1/2)."""
+    from numerics import subnormal_bf16
+    n = 256
+    inp = synth.host_inputs(n, seed=8, p=1.0)
+    x, kv = inp["x"], inp["kv"]
+    x[0:32] = subnormal_bf16(x[0:32])
+    kv[0:32, 4 * 5120:] = 0
+    x[32:64] = 0
+    kv[32:64, 4 * 5120:] = subnormal_bf16(kv[32:64, 4 * 5120:])
+    st, out, saved = _run_and_check(gpu, inp)
+    assert np.array_equal(out[0:32], x[0:32]), "subnormal X not carried to out"
+    assert np.all(saved[32:64, :, 0] == 0.5) and np.all(saved[32:64, :, 1] == 0.0)
+    v = inp["kv"][32:64, 4 * 5120:]
+    half = ((v.astype(np.uint32) << 16).view(np.float32).astype(np.float64) * 0.5)
+    import oracle
+    want = oracle.round_bf16(np.broadcast_to(half[:, None, :], (32, 4, 5120)))
+    assert np.array_equal(out[32:64], want), "v / 2 of a subnormal value row"
+    print(st)
+
+
 def test_fwd_n8192_mask09(gpu):
     """N = 8192, mask Bernoulli(0.9): every element compared."""
     inp = synth.host_inputs(8192, seed=0, p=0.9)
