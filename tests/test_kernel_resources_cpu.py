@@ -76,3 +76,16 @@ def test_backward_main_kernel_occupancy(resources):
     (main,) = [r for k, r in resources["engram_bwd.hip"].items() if "engram_bwd_main_kernel" in k]
     assert main["Occupancy [waves/SIMD]"] >= 2, main
     assert main["VGPRs"] <= 256, main
+
+
+def test_gateconv_backward_occupancy(resources):
+    """The GateConv chunk rule sizes the backward's grid for the workgroups a
+    CU holds at once: two of the conv kernel's 4-wave workgroups at d = 2560
+    (256 x 10 map) and two of its 12-wave ones at d = 1536 (768 x 2 map), and
+    one 8-wave workgroup at d = 5120.  Occupancy here is waves per SIMD (a CU
+    has four SIMDs), so those need 2, 6 and 2 waves per SIMD."""
+    conv = {k: r for k, r in resources["engram_gateconv.hip"].items() if "gateconv_bwd_conv_kernel" in k}
+    want = {"ColMapILi256ELi10E": 2, "ColMapILi768ELi2E": 6, "ColMapILi512ELi10E": 2}
+    for tag, waves in want.items():
+        (r,) = [r for k, r in conv.items() if tag in k]
+        assert r["Occupancy [waves/SIMD]"] >= waves, (tag, r)
