@@ -101,14 +101,16 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   const int64_t b = (int64_t)(bi >> 5) * 8 + r;
   if (b >= rows) return;  // rows are padded to a multiple of 8
 
-  for (int j = threadIdx.x; j < kHidden / 4; j += kBwdThreads)
-    wrow[j & 1][j >> 1] = reinterpret_cast<const f32x4*>(weight + s * kHidden)[j];
-  float acc[kBwdVecs][kVec];
+  // The stream's weight row is loaded first and written to LDS only after the
+  // first token's loads have been issued (below): the wait for it then leaves
+  // those in flight, and the kernel's start pays one memory latency, not two.
+  constexpr int kWeightLoads = (kHidden / 4 + kBwdThreads - 1) / kBwdThreads;
+  f32x4 wt[kWeightLoads];
 #pragma unroll
-  for (int v = 0; v < kBwdVecs; ++v)
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) acc[v][e] = 0.f;
-  __syncthreads();
+  for (int q = 0; q < kWeightLoads; ++q) {
+    const int j = threadIdx.x + q * kBwdThreads;
+    if (j < kHidden / 4) wt[q] = reinterpret_cast<const f32x4*>(weight + s * kHidden)[j];
+  }
 
   // the saved row (gate, dot, rstd_X, rstd_key of each stream; 64 bytes) of
   // this slot's next token, fetched one token ahead through the scalar cache
@@ -191,6 +193,17 @@ engram_bwd_main_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   for (int so = 0; so < kStreams; ++so) sv[so] = svn[so];
   Flags fl = flags_of(sv, 0);
   issue(L, token(0), fl, true);
+#pragma unroll
+  for (int q = 0; q < kWeightLoads; ++q) {
+    const int j = threadIdx.x + q * kBwdThreads;
+    if (j < kHidden / 4) wrow[j & 1][j >> 1] = wt[q];
+  }
+  float acc[kBwdVecs][kVec];
+#pragma unroll
+  for (int v = 0; v < kBwdVecs; ++v)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) acc[v][e] = 0.f;
+  __syncthreads();  // the weight row in LDS
   for (int jj = 0; jj < steps; ++jj) {
     const int64_t t = token(jj);
     const bool more = jj + 1 < steps;
