@@ -17,8 +17,11 @@ constexpr int64_t kXRowBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 2;  // 
 constexpr int64_t kKvRowBytes = (int64_t)ENGRAM_KV_COLS * 2;                 // 51200
 constexpr int64_t kWeightBytes = (int64_t)ENGRAM_STREAMS * ENGRAM_HIDDEN * 4;  // 81920
 constexpr int64_t kSavedRowBytes = (int64_t)ENGRAM_STREAMS * 4 * 4;          // 64
-// one resident per CU, the rest queued: of 1, 2, 4 and 8 per CU, timed cold, the
-// fastest at N = 8192 and within 1% of the fastest at N = 1,048,512
+// forward workgroups per CU, one resident, the rest queued: of 1, 2, 4 and 8,
+// timed cold, the fastest at N = 8192 and within 1% of the fastest at
+// N = 1,048,512; back to back in the forward + backward step 8 was 0.3%
+// faster, less than the step moves with where the buffers land, and 16 or
+// 32 were 2-4% slower
 constexpr int kFwdWorkgroupsPerCu = 4;
 constexpr int kMaxDevices = 64;
 
