@@ -56,7 +56,7 @@ def empty_f32(shape, gpu):
     return poison(torch.empty(shape, dtype=torch.float32, device=gpu))
 
 
-def run_fwd(inp, gpu):
+def run_fwd(inp, gpu, eps=EPS):
     import torch
     import memory_bound_engram_amd as eg
     M, T, d = inp["H"].shape
@@ -64,7 +64,7 @@ def run_fwd(inp, gpu):
     wh, wv, cw = dev(inp["wh"], gpu), dev(inp["wv"], gpu), dev(inp["cw"], gpu)
     Y, vhat = empty_bf16((M, T, d), gpu), empty_bf16((M, T, d), gpu)
     al, rh, rk, rv = (empty_f32((M, T), gpu) for _ in range(4))
-    eg.engram_gateconv_fwd(H, k, v, wh, wv, cw, Y, vhat, al, rh, rk, rv, eps=EPS)
+    eg.engram_gateconv_fwd(H, k, v, wh, wv, cw, Y, vhat, al, rh, rk, rv, eps=eps)
     torch.cuda.synchronize()
     from gpu_util import u16
     return {"Y": u16(Y), "vhat": u16(vhat), "alpha": al.cpu().numpy(), "rh": rh.cpu().numpy(),
@@ -90,10 +90,10 @@ def run_bwd(inp, saved, gpu, repeat=1):
     return outs if repeat > 1 else outs[0]
 
 
-def oracle_fwd(inp):
+def oracle_fwd(inp, eps=EPS):
     H, k, v = f64(inp["H"]), f64(inp["k"]), f64(inp["v"])
     wh, wv, cw = (inp[x].astype(np.float64) for x in ("wh", "wv", "cw"))
-    return oracle.gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=EPS, mags=True)
+    return oracle.gateconv_fwd_f64(H, k, v, wh, wv, cw, eps=eps, mags=True)
 
 
 def rounded_saved(ref):
@@ -168,6 +168,19 @@ def test_gateconv_fwd_parity(gpu, M, T, d):
 def test_gateconv_bwd_parity(gpu, M, T, d):
     inp = synth.gateconv_inputs(M, T, d, seed=M * 1000 + T + 7, edge=True)
     saved = rounded_saved(oracle_fwd(inp))
+    check_bwd(run_bwd(inp, saved, gpu), oracle_bwd(inp, saved))
+
+
+@pytest.mark.parametrize("eps", [1e-3, 0.25])
+def test_gateconv_other_eps(gpu, eps):
+    """The norms' eps is a runtime argument (the page's default is 1e-6):
+    other values reach the kernels' rrms_h, rrms_k and rrms_v, checked in
+    full against the oracle with the same eps, and the backward runs on
+    that forward's saved tensors."""
+    inp = synth.gateconv_inputs(2, 45, 1536, seed=31)
+    ref = oracle_fwd(inp, eps=eps)
+    check_fwd(inp, run_fwd(inp, gpu, eps=eps), ref)
+    saved = rounded_saved(ref)
     check_bwd(run_bwd(inp, saved, gpu), oracle_bwd(inp, saved))
 
 
