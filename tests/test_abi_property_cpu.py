@@ -52,13 +52,13 @@ def _no_gpu():
 
 
 @st.composite
-def _layout(draw, names, nullable):
-    """Fake 16-byte-aligned addresses in 24 slots (so some buffers share a slot
-    and overlap), then at most one fault: a NULL (among `nullable`) or a
+def _layout(draw, names, nullable, slots=24):
+    """Fake 16-byte-aligned addresses in `slots` slots (so some buffers share a
+    slot and overlap), then at most one fault: a NULL (among `nullable`) or a
     misaligned pointer."""
     a = {}
     for k in names:
-        a[k] = BASE + draw(st.integers(0, 23)) * SPAN + 16 * draw(st.integers(0, 1 << 16))
+        a[k] = BASE + draw(st.integers(0, slots - 1)) * SPAN + 16 * draw(st.integers(0, 1 << 16))
     fault = draw(st.sampled_from(["none"] * 4 + ["null", "align"]))
     k = draw(st.sampled_from(names))
     if fault == "null" and k in nullable:
@@ -158,3 +158,78 @@ def test_the_model_accepts_some_and_rejects_each_way():
     assert _fwd_model(dict(ok, m=ok["m"] + 1), 8) == ACCEPT  # the mask needs no alignment
     assert _fwd_model(dict(ok, out=ok["out"] + 8), 8) == eg.ERR_ALIGN
     assert _fwd_model(dict(ok, sv=ok["x"] + XB), 8) == eg.ERR_OVERLAP
+
+
+# ---------------- GateConv ("Engram Operators", GateConv section) ----------------
+
+_GC_FWD = ("H", "k", "v", "wh", "wv", "cw", "Y", "vhat", "alpha", "rh", "rk", "rv")
+_GC_BWD = ("dY", "H", "k", "v", "wh", "wv", "cw", "vhat", "alpha", "rh", "rk", "rv",
+           "dH", "dk", "dv", "dwh", "dwv", "dcw", "ws")
+_GC_VALID = st.tuples(st.integers(1, 8), st.integers(1, 600), st.integers(1, 10).map(lambda q: 512 * q))
+_GC_DIMS = st.one_of(
+    _GC_VALID, _GC_VALID, _GC_VALID,
+    st.tuples(st.integers(-1, 3), st.integers(-1, 3), st.sampled_from([0, 511, 512, 640, 5120, 5632])),
+    st.sampled_from([(1024, 4097, 512), (4194305, 1, 512), (1, 4194305, 512), (2048, 2048, 512)]))
+
+
+def _gc_dims_ok(M, T, d):
+    return (1 <= M <= eg.GATECONV_ROWS_MAX and 1 <= T <= eg.GATECONV_ROWS_MAX and M * T <= eg.GATECONV_ROWS_MAX
+            and 512 <= d <= eg.GATECONV_D_MAX and d % 512 == 0)
+
+
+def _gc_fwd_model(a, M, T, d, eps):
+    if any(a[k] is None for k in _GC_FWD):
+        return eg.ERR_NULL
+    if not _gc_dims_ok(M, T, d) or not (0.0 <= eps <= 1.0):
+        return eg.ERR_N_RANGE
+    if any(a[k] % 16 for k in _GC_FWD):
+        return eg.ERR_ALIGN
+    tb, sb = M * T * d * 2, M * T * 4
+    ins = [_rng(a["H"], tb), _rng(a["k"], tb), _rng(a["v"], tb), _rng(a["wh"], 4 * d), _rng(a["wv"], 4 * d),
+           _rng(a["cw"], 16 * d)]
+    outs = [_rng(a["Y"], tb), _rng(a["vhat"], tb)] + [_rng(a[k], sb) for k in ("alpha", "rh", "rk", "rv")]
+    return eg.ERR_OVERLAP if _any_overlap(ins, outs) else ACCEPT
+
+
+def _gc_bwd_model(a, M, T, d):
+    if any(a[k] is None for k in _GC_BWD):
+        return eg.ERR_NULL
+    if not _gc_dims_ok(M, T, d):
+        return eg.ERR_N_RANGE
+    if any(a[k] % 16 for k in _GC_BWD):
+        return eg.ERR_ALIGN
+    tb, sb = M * T * d * 2, M * T * 4
+    ins = ([_rng(a[k], tb) for k in ("dY", "H", "k", "v")] + [_rng(a["wh"], 4 * d), _rng(a["wv"], 4 * d),
+           _rng(a["cw"], 16 * d), _rng(a["vhat"], tb)] + [_rng(a[k], sb) for k in ("alpha", "rh", "rk", "rv")])
+    outs = ([_rng(a[k], tb) for k in ("dH", "dk", "dv")] + [_rng(a["dwh"], 4 * d), _rng(a["dwv"], 4 * d),
+            _rng(a["dcw"], 16 * d), _rng(a["ws"], eg.engram_gateconv_bwd_workspace_bytes(M, T, d))])
+    return eg.ERR_OVERLAP if _any_overlap(ins, outs) else ACCEPT
+
+
+@settings(max_examples=500, deadline=None)
+@given(st.data())
+def test_gateconv_fwd_validation_matches_the_model(data):
+    a = data.draw(_layout(_GC_FWD, _GC_FWD, slots=48), label="layout")
+    M, T, d = data.draw(_GC_DIMS, label="M, T, d")
+    eps = data.draw(st.sampled_from([1e-6, 0.0, 1.0, 0.5, -1e-6, 1.5, float("nan"), float("inf")]), label="eps")
+    want = _gc_fwd_model(a, M, T, d, eps)
+    if want == ACCEPT:
+        if not _no_gpu():
+            return
+        want = eg.ERR_LAUNCH
+    got = eg.lib.engram_gateconv_fwd(*(a[k] for k in _GC_FWD), M, T, d, eps, None)
+    assert got == want, (a, M, T, d, eps)
+
+
+@settings(max_examples=500, deadline=None)
+@given(st.data())
+def test_gateconv_bwd_validation_matches_the_model(data):
+    a = data.draw(_layout(_GC_BWD, _GC_BWD, slots=96), label="layout")
+    M, T, d = data.draw(_GC_DIMS, label="M, T, d")
+    want = _gc_bwd_model(a, M, T, d)
+    if want == ACCEPT:
+        if not _no_gpu():
+            return
+        want = eg.ERR_LAUNCH
+    got = eg.lib.engram_gateconv_bwd(*(a[k] for k in _GC_BWD), M, T, d, None)
+    assert got == want, (a, M, T, d)
