@@ -141,3 +141,31 @@ def test_autograd_pins_alone_reject_mutant(desc, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_autograd_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"autograd pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
+
+
+# The mistakes that the invariance properties of the gate (masking, power-of-two
+# scales, key negation, stream order, Euler's orthogonality) catch on their own,
+# with no expected value at all.  The special cases (the clamp, sgn(0), eps),
+# the rounding mode and the weight's product rule are left to the fixed pins.
+PROPERTY_CAUGHT = [
+    "dx drops the dot term", "dk wrong sign", "dk transposed operand", "dx missing 1/d", "dw uses x^ twice",
+    "dz drops (1 - gate)", "rstd without the mean", "saved rstd fields swapped", "masked token saves the raw gate",
+    "mask ignored in the output", "value gradient reads stream 0 only", "value taken from the last key block",
+    "dot over raw (unnormalised) key",
+]
+
+
+@pytest.mark.parametrize("desc", PROPERTY_CAUGHT)
+def test_property_pins_alone_reject_mutant(desc, tmp_path):
+    pytest.importorskip("hypothesis")
+    (old, new), = [(o, n) for dsc, o, n in MUTANTS if dsc == desc]
+    mutant = tmp_path / "mutant.c"
+    mutant.write_text(open(SRC).read().replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                           str(lib), str(mutant), "-lm", "-lpthread"])
+    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_property_cpu.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"property pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
