@@ -143,15 +143,21 @@ def test_autograd_pins_alone_reject_mutant(desc, tmp_path):
     assert r.returncode != 0, f"autograd pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
 
 
-# The mistakes that the invariance properties of the gate (masking, power-of-two
-# scales, key negation, stream order, Euler's orthogonality) catch on their own,
-# with no expected value at all.  The special cases (the clamp, sgn(0), eps),
-# the rounding mode and the weight's product rule are left to the fixed pins.
+# The mistakes that the invariance properties catch on their own, with no
+# expected value at all: for the gate, masking, power-of-two scales, key
+# negation, stream order and Euler's orthogonality (the special cases -- the
+# clamp, sgn(0), eps --, the rounding mode and the weight's product rule are
+# left to the fixed pins); for GateConv, row scales of H, k and v, the H-k
+# exchange, the sign of rms_w_h, the rms_w_v-conv_w trade and Euler's
+# relations (the conv's tap order, the 1/sqrt(d) scale, the SiLU derivative
+# and the two identical halves of drms_w_h are left to the fixed pins).
 PROPERTY_CAUGHT = [
     "dx drops the dot term", "dk wrong sign", "dk transposed operand", "dx missing 1/d", "dw uses x^ twice",
     "dz drops (1 - gate)", "rstd without the mean", "saved rstd fields swapped", "masked token saves the raw gate",
     "mask ignored in the output", "value gradient reads stream 0 only", "value taken from the last key block",
     "dot over raw (unnormalised) key",
+    "gateconv key normalised with w_v", "gateconv residual dropped", "gateconv backward conv runs causally",
+    "gateconv rms_v backward sign", "gateconv dv misses alpha", "gateconv dcw pairs the wrong token",
 ]
 
 
@@ -166,6 +172,7 @@ def test_property_pins_alone_reject_mutant(desc, tmp_path):
                            str(lib), str(mutant), "-lm", "-lpthread"])
     env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_property_cpu.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_property_cpu.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_gateconv_property_cpu.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"property pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
