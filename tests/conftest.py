@@ -8,6 +8,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+try:  # property-based tests draw the same cases on every run, so a run is reproducible
+    from hypothesis import settings as _hyp_settings
+    _hyp_settings.register_profile("repro", derandomize=True, database=None)
+    _hyp_settings.load_profile("repro")
+except ImportError:
+    pass
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
