@@ -127,6 +127,68 @@ def test_bwd_all_masked(gpu):
     assert not f32(gw).any()
 
 
+def _keys_scaled(kv, k):
+    """The four key blocks of bf16 KV rows times 2^k, exactly; the value stays."""
+    out = kv.copy()
+    f = (kv[:, :4 * 5120].astype(np.uint32) << 16).view(np.float32)
+    g = f * np.float32(2.0 ** k)
+    out[:, :4 * 5120] = (g.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((out[:, :4 * 5120].astype(np.uint32) << 16).view(np.float32), g), "scale not exact"
+    return out
+
+
+def test_bwd_all_clamp_n8192(gpu):
+    """N = 8192 (64 rows of 128 tokens), every key times 2^-64: its squares
+    fall far below eps, so rstd_key ~ eps^-1/2 leaves the normalised key ~1e-9
+    and |dot| < 1e-6 on every stream of every token.  Every unmasked token
+    takes the clamp path (delta = 0): grad_x = G bit for bit, grad_key = +0,
+    grad_weight = 0, and grad_value = sum_s gate_s G_s alone, against the
+    oracle on its saved state and on the device's own."""
+    import torch
+    from gpu_util import dev_inputs, f32, run_bwd, run_fwd, u16
+    from numerics import bf16_to_f64
+    from parity import check_bwd_end_to_end, check_fwd
+    n = 8192
+    inp = synth.host_inputs(n, seed=5, p=0.9, grad=True)
+    inp["kv"] = _keys_scaled(inp["kv"], -64)
+    st_b, saved_ref, *_ = _bwd_case(gpu, inp, threads=16)
+    assert np.all(np.abs(saved_ref[:, :, 1]) < np.float32(1e-6))
+    d = dev_inputs(inp, gpu)
+    out, saved = run_fwd(d)
+    gx, gkv, gw = run_bwd(d, saved)
+    torch.cuda.synchronize()
+    sv = f32(saved)
+    assert np.all(np.abs(sv[:, :, 1]) < np.float32(1e-6)), "a stream left the clamp path"
+    assert np.array_equal(u16(gx), inp["grad_out"]), "grad_x is not G"
+    assert not u16(gkv)[:, :4 * 5120].any(), "grad_key is not +0"
+    assert not f32(gw).any(), "grad_weight is not 0"
+    on = inp["mask"] != 0
+    assert np.any(bf16_to_f64(u16(gkv)[on, 4 * 5120:]) != 0.0)
+    fwd_ref = oracle.fwd_bf16(inp["x"], inp["kv"], inp["weight"], inp["mask"], threads=16, extras=True)
+    st_f = check_fwd(inp, u16(out), sv, ref=fwd_ref)
+    st_e = check_bwd_end_to_end(inp, sv, u16(gx), u16(gkv), f32(gw), fwd_ref, threads=16)
+    print(st_f, st_b, st_e)
+
+
+def test_bwd_all_masked_n8192(gpu):
+    """Every token masked at N = 8192 (64 rows of 128 tokens): grad_x = G bit
+    for bit, grad_kv = +0, grad_weight = 0."""
+    import torch
+    from gpu_util import dev_inputs, f32, run_bwd, run_fwd, u16
+    n = 8192
+    inp = synth.host_inputs(n, seed=6, p=0.0, grad=True)
+    assert not inp["mask"].any()
+    d = dev_inputs(inp, gpu)
+    out, saved = run_fwd(d)
+    gx, gkv, gw = run_bwd(d, saved)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out), inp["x"])
+    assert np.all(f32(saved)[:, :, 0] == 0.0)
+    assert np.array_equal(u16(gx), inp["grad_out"])
+    assert not u16(gkv).any()
+    assert not f32(gw).any()
+
+
 def test_fwd_bwd_repeated_1000_bitwise(gpu):
     """N = 8192 with the edge-row recipe, mask 0.3: 1000 forward+backward
     launches back to back on one stream; the last results equal the first
