@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -95,22 +96,37 @@ MUTANTS = [
 ]
 
 
-@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_reject_mutant(desc, old, new, tmp_path):
+PIN_FILES = ("test_oracle_pins.py", "test_oracle_gateconv_pins.py", "test_oracle_tolerance_scales.py")
+WORKERS = max(1, min(8, os.cpu_count() or 1))
+
+
+def _missed(descs, files_for, tmp_path):
+    """Build each named mutant of the oracle and run `files_for(desc)` against
+    it in a child pytest (isolated: a mutant may read out of bounds); up to
+    WORKERS children at a time.  Returns the mutants whose pins all passed."""
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
-    mutant = tmp_path / "mutant.c"
-    mutant.write_text(src.replace(old, new))
-    lib = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
-                           str(lib), str(mutant), "-lm", "-lpthread"])
-    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_gateconv_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_tolerance_scales.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
+    table = {m[0]: m for m in MUTANTS}
+
+    def one(i, desc):
+        _, old, new = table[desc]
+        assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+        mutant, lib = tmp_path / f"mutant{i}.c", tmp_path / f"libmutant{i}.so"
+        mutant.write_text(src.replace(old, new))
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
+                               str(lib), str(mutant), "-lm", "-lpthread"])
+        env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib), PYTEST_DISABLE_PLUGIN_AUTOLOAD="1")
+        r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                            *[os.path.join(ROOT, "tests", f) for f in files_for(desc)]],
+                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+        return desc if r.returncode == 0 else None
+
+    with ThreadPoolExecutor(max_workers=WORKERS) as pool:
+        return [d for d in pool.map(one, range(len(descs)), descs) if d is not None]
+
+
+def test_pins_reject_every_mutant(tmp_path):
+    missed = _missed([m[0] for m in MUTANTS], lambda desc: PIN_FILES, tmp_path)
+    assert not missed, f"the pins did not catch: {missed}"
 
 
 # The mistakes in the method's own arithmetic (forward and backward of the gate
@@ -128,19 +144,9 @@ AUTOGRAD_CAUGHT = [
 ]
 
 
-@pytest.mark.parametrize("desc", AUTOGRAD_CAUGHT)
-def test_autograd_pins_alone_reject_mutant(desc, tmp_path):
-    (old, new), = [(o, n) for dsc, o, n in MUTANTS if dsc == desc]
-    mutant = tmp_path / "mutant.c"
-    mutant.write_text(open(SRC).read().replace(old, new))
-    lib = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
-                           str(lib), str(mutant), "-lm", "-lpthread"])
-    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_autograd_pins.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"autograd pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
+def test_autograd_pins_alone_reject_mutants(tmp_path):
+    missed = _missed(AUTOGRAD_CAUGHT, lambda desc: ("test_oracle_autograd_pins.py",), tmp_path)
+    assert not missed, f"the autograd pins alone did not catch: {missed}"
 
 
 # The mistakes that the invariance properties catch on their own, with no
@@ -161,18 +167,8 @@ PROPERTY_CAUGHT = [
 ]
 
 
-@pytest.mark.parametrize("desc", PROPERTY_CAUGHT)
-def test_property_pins_alone_reject_mutant(desc, tmp_path):
+def test_property_pins_alone_reject_mutants(tmp_path):
     pytest.importorskip("hypothesis")
-    (old, new), = [(o, n) for dsc, o, n in MUTANTS if dsc == desc]
-    mutant = tmp_path / "mutant.c"
-    mutant.write_text(open(SRC).read().replace(old, new))
-    lib = tmp_path / "libmutant.so"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-o",
-                           str(lib), str(mutant), "-lm", "-lpthread"])
-    env = dict(os.environ, ENGRAM_ORACLE_LIB=str(lib))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_property_cpu.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_gateconv_property_cpu.py")],
-                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"property pins did not catch mutant '{desc}':\n{r.stdout[-2000:]}"
+    missed = _missed(PROPERTY_CAUGHT, lambda desc: ("test_oracle_gateconv_property_cpu.py" if desc.startswith("gateconv")
+                                                    else "test_oracle_property_cpu.py",), tmp_path)
+    assert not missed, f"the property pins alone did not catch: {missed}"
