@@ -2,8 +2,8 @@
 
 The fp64 oracle (oracle/engram_oracle.c) and the host input generator
 (synth/synth_host.c) are rebuilt with gcc and -fsanitize=address,undefined
-in a temporary directory, and the oracle, tolerance-scale, GateConv and
-generator pin suites run against those builds in a child process with the
+in a temporary directory, and the oracle, tolerance-scale, GateConv,
+random-case property and generator pin suites run against those builds in a child process with the
 sanitizer runtimes preloaded (the Python interpreter itself is not
 instrumented).  Any out-of-bounds access, use after free or undefined
 operation in the C code aborts the child; the test also refuses a run whose
@@ -48,6 +48,8 @@ def test_oracle_and_generator_clean_under_asan_ubsan(tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_tolerance_scales.py"),
                         os.path.join(ROOT, "tests", "test_oracle_gateconv_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_property_cpu.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_gateconv_property_cpu.py"),
                         os.path.join(ROOT, "tests", "test_synth.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=1200)
     out = r.stdout + r.stderr
