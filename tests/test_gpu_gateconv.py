@@ -155,7 +155,10 @@ def oracle_bwd(inp, saved):
 # 512 workgroups (563 at d = 512, 625 at d = 2048), where the weight gradients
 # are summed in two levels and the last block of 64 partial rows is ragged.
 SHAPES = [(2, 37, 5120), (3, 5, 1024), (1, 1, 512), (5, 300, 2048), (7, 3, 3072), (1, 2, 4096), (2, 700, 1536),
-          (2, 70, 4608), (3, 33, 2560), (1, 129, 3584), (2, 45, 512), (3, 3000, 512), (1, 20000, 2048)]
+          (2, 70, 4608), (3, 33, 2560), (1, 129, 3584), (2, 45, 512), (3, 3000, 512), (1, 20000, 2048),
+          # many sequences no longer than the conv window: every chunk crosses hundreds of sequence
+          # starts and every row's dc window runs past its sequence's end
+          (2000, 1, 5120), (1200, 2, 1024), (600, 4, 2560)]
 
 
 @pytest.mark.parametrize("M,T,d", SHAPES)
