@@ -412,6 +412,30 @@ def measure_config(torch, synth, eg, dev, stream, c, rotate):
     return line
 
 
+SWEEP_FWD = (64, 256, 1024, 2048, 4096, 8192, 32768, 131072, 524288, N_LARGE)
+SWEEP_STEP = (64, 256, 1024, 2048, 4096, 8192)
+
+
+def bench_sweep(torch, synth, eg, dev, stream, rotate):
+    """Throughput against the token count: the forward alone, and forward +
+    backward (the backward's accepted sizes), each timed as in
+    measure_config (calls back to back, rotating buffer sets while they fit
+    in about 100 GB); one JSON line per size."""
+    # device bytes of one buffer set per token: inputs and outputs (the backward's
+    # grad_out, grad_x and grad_kv on top of the forward's)
+    per_token = {"fwd": fwd_bytes(1) + 40960 + 64, "fwd+bwd": fwd_bytes(1) + bwd_bytes(1) + 3 * 40960 + 51200}
+    for op, sizes in (("fwd", SWEEP_FWD), ("fwd+bwd", SWEEP_STEP)):
+        for n in sizes:
+            fit = max(1, int(100e9 // (per_token[op] * n)))
+            c = dict(config=-1, op=op, tokens=n, mask_p=0.9, edge=False,
+                     # about 0.2 s of calls at 6 TB/s, 5 to 200 of them
+                     launches=max(5, min(200, int(1.2e12 // (fwd_bytes(n) + (bwd_bytes(n) if op != "fwd" else 0))))),
+                     desc=f"{op}, N={n}, mask Bernoulli(0.9)")
+            line = measure_config(torch, synth, eg, dev, stream, c, min(rotate, fit))
+            line.pop("config")
+            print(json.dumps(line), flush=True)
+
+
 def bench_configs(torch, synth, eg, dev, stream, with_cpu, rotate):
     """One JSON line per configuration (measure_config), with the oracle's
     rate on a bounded sample beside it."""
@@ -686,6 +710,9 @@ def main():
                          "finds its data in cache from the previous one")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the benchmark line, one line per workload configuration (0-4)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the benchmark line, throughput against N for the forward and for "
+                         "forward + backward (one JSON line per size)")
     ap.add_argument("--placement", action="store_true",
                     help="instead of the benchmark line, the N=1,048,512 forward under several "
                          "placements of its tensors (one JSON line each)")
@@ -727,6 +754,9 @@ def main():
         return
     if args.placement:
         bench_placement(torch, synth, eg, dev, torch.cuda.current_stream(dev))
+        return
+    if args.sweep:
+        bench_sweep(torch, synth, eg, dev, torch.cuda.current_stream(dev), max(1, args.rotate))
         return
     if args.configs:
         bench_configs(torch, synth, eg, dev, torch.cuda.current_stream(dev), not args.no_cpu, max(1, args.rotate))
