@@ -92,6 +92,12 @@ typedef enum {
  *   N      1 <= N <= 4194240
  * No workspace.  A false mask byte makes out[t] a bit copy of x[t] and saves
  * gate 0 for every stream of t; dot and both rstd are still saved.
+ * Calls with N > 16384 keep their workgroups in step with counters in a small
+ * device array of the library (16 slots per GPU, one taken per call round
+ * robin, each set back to zero by the call that used it).  They only pace the
+ * kernel: results never depend on them, and every wait on them is bounded, so
+ * more than 16 such calls in flight at once on one GPU (sharing a slot) can
+ * run slower but not differently or forever.
  */
 engram_status engram_gate_fwd(const void *x, const void *kv, const float *weight, const uint8_t *mask,
                               void *out, float *saved, int64_t N, void *stream);

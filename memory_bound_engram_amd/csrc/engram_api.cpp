@@ -88,6 +88,8 @@ engram_status engram_gate_fwd(const void* x, const void* kv, const float* weight
                       range_of(mask, N)};
   const Range outs[] = {range_of(out, N * kXRowBytes), range_of(saved, saved ? N * kSavedRowBytes : 0)};
   if (any_overlap(in, 4, outs, 2)) return ENGRAM_ERR_OVERLAP;
+  if (N > engram::kFwdPacedMinTokens)  // one workgroup per CU, epochs with a bounded-wait barrier between them
+    return launched(engram::launch_fwd_paced(x, kv, weight, mask, out, saved, N, cu_count(), (hipStream_t)stream));
   int64_t grid = (int64_t)kFwdWorkgroupsPerCu * cu_count();
   if (grid > N) grid = N;
   return launched(engram::launch_fwd(x, kv, weight, mask, out, saved, N, (int)grid, (hipStream_t)stream));

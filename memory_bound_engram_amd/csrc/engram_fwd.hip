@@ -24,22 +24,88 @@
 #include "engram_device.h"
 #include "engram_launch.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace engram {
 
 constexpr int kFwdThreads = 64 * kStreams;   // one wave per stream
 constexpr int kFwdVecs = kRowVecs / 64;      // 10 vectors per lane per row
 
-// kSave = false is the inference forward: saved is not written; out is
-// bit-identical to the saving path (same arithmetic).
+// One token of the forward: the four waves of the workgroup each handle their
+// stream of token t.  kSave = false is the inference forward: saved is not
+// written; out is bit-identical to the saving path (same arithmetic).
 template <bool kSave>
-__global__ void __launch_bounds__(kFwdThreads)
-engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
-                  const float* __restrict__ weight, const uint8_t* __restrict__ mask,
-                  uint16_t* __restrict__ out, float* __restrict__ saved, int64_t n) {
-  const int s = threadIdx.x >> 6;     // stream of this wave
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void fwd_token(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
+                                          const uint8_t* __restrict__ mask, uint16_t* __restrict__ out,
+                                          float* __restrict__ saved, const float (&w)[kFwdVecs][kVec], int64_t t,
+                                          int s, int lane) {
+  const bool m = mask[t] != 0;
+  const uint16_t* xs = x + t * (kStreams * kHidden) + s * kHidden;
+  const uint16_t* ks = kv + t * kKvCols + s * kHidden;
+  const uint16_t* vs = kv + t * kKvCols + kValueCol;
 
-  float w[kFwdVecs][kVec];
+  u32x4 xr[kFwdVecs], kr[kFwdVecs], vr[kFwdVecs];
+#pragma unroll
+  for (int i = 0; i < kFwdVecs; ++i) {
+    const int col = (lane + 64 * i) * kVec;
+    xr[i] = load16_stream(xs + col);
+    kr[i] = load16_stream(ks + col);
+  }
+  if (m) {  // masked tokens never need the value
+#pragma unroll
+    for (int i = 0; i < kFwdVecs; ++i) vr[i] = load16(vs + (lane + 64 * i) * kVec);
+  }
+
+  float sxx = 0.f, skk = 0.f, sxwk = 0.f;
+#pragma unroll
+  for (int i = 0; i < kFwdVecs; ++i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = bf_lo(xr[i][q]), x1 = bf_hi(xr[i][q]);
+      const float k0 = bf_lo(kr[i][q]), k1 = bf_hi(kr[i][q]);
+      sxx = fmaf(x0, x0, sxx);
+      sxx = fmaf(x1, x1, sxx);
+      skk = fmaf(k0, k0, skk);
+      skk = fmaf(k1, k1, skk);
+      sxwk = fmaf(x0 * w[i][2 * q], k0, sxwk);
+      sxwk = fmaf(x1 * w[i][2 * q + 1], k1, sxwk);
+    }
+  }
+  sxx = read_lane(wave_sum_to_lane63(sxx), 63);
+  skk = read_lane(wave_sum_to_lane63(skk), 63);
+  sxwk = read_lane(wave_sum_to_lane63(sxwk), 63);
+
+  const float rx = 1.0f / sqrtf(sxx / (float)kHidden + kEps);
+  const float rk = 1.0f / sqrtf(skk / (float)kHidden + kEps);
+  const float dot = (sxwk * rx) * rk;
+  const float mag = sqrtf(fmaxf(fabsf(dot), kClamp));
+  const float z = dot > 0.f ? mag : (dot < 0.f ? -mag : 0.f);
+  const float gate = 1.0f / (1.0f + expf(-z));
+
+  uint16_t* os = out + t * (kStreams * kHidden) + s * kHidden;
+#pragma unroll
+  for (int i = 0; i < kFwdVecs; ++i) {
+    u32x4 o = xr[i];
+    if (m) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float o0 = fmaf(gate, bf_lo(vr[i][q]), bf_lo(xr[i][q]));
+        const float o1 = fmaf(gate, bf_hi(vr[i][q]), bf_hi(xr[i][q]));
+        o[q] = pack_bf16x2(o0, o1);
+      }
+    }
+    store16_stream(os + (lane + 64 * i) * kVec, o);
+  }
+  if (kSave && lane == 0) {
+    const f32x4 sv = {m ? gate : 0.f, dot, rx, rk};
+    *reinterpret_cast<f32x4*>(saved + t * (kStreams * 4) + 4 * s) = sv;
+  }
+}
+
+// Each lane's slice of the stream's weight row (10 x 8 fp32), kept in VGPRs.
+__device__ __forceinline__ void load_weight_slice(const float* __restrict__ weight, float (&w)[kFwdVecs][kVec], int s,
+                                                  int lane) {
 #pragma unroll
   for (int i = 0; i < kFwdVecs; ++i) {
     const int col = (lane + 64 * i) * kVec;
@@ -51,68 +117,113 @@ engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ k
       w[i][4 + e] = b[e];
     }
   }
+}
 
-  for (int64_t t = blockIdx.x; t < n; t += gridDim.x) {
-    const bool m = mask[t] != 0;
-    const uint16_t* xs = x + t * (kStreams * kHidden) + s * kHidden;
-    const uint16_t* ks = kv + t * kKvCols + s * kHidden;
-    const uint16_t* vs = kv + t * kKvCols + kValueCol;
+template <bool kSave>
+__global__ void __launch_bounds__(kFwdThreads)
+engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
+                  const float* __restrict__ weight, const uint8_t* __restrict__ mask,
+                  uint16_t* __restrict__ out, float* __restrict__ saved, int64_t n) {
+  const int s = threadIdx.x >> 6;     // stream of this wave
+  const int lane = threadIdx.x & 63;
+  float w[kFwdVecs][kVec];
+  load_weight_slice(weight, w, s, lane);
+  for (int64_t t = blockIdx.x; t < n; t += gridDim.x) fwd_token<kSave>(x, kv, mask, out, saved, w, t, s, lane);
+}
 
-    u32x4 xr[kFwdVecs], kr[kFwdVecs], vr[kFwdVecs];
-#pragma unroll
-    for (int i = 0; i < kFwdVecs; ++i) {
-      const int col = (lane + 64 * i) * kVec;
-      xr[i] = load16_stream(xs + col);
-      kr[i] = load16_stream(ks + col);
+// ---- the paced forward, for long calls ----
+//
+// A long call is walked in epochs: one workgroup per CU (all resident at
+// once), workgroup b taking tokens b + G i (G = grid size), and after every
+// kFwdEpochSteps of them the workgroups wait for each other at a soft barrier
+// before the next epoch.  Workgroups that run one long strided loop drift
+// apart, so that at any moment some of them read while others write; kept
+// together, the chip reads a band of tokens, then writes it.  Measured on
+// MI355X at N = 1,048,512 (one set of buffers): the unpaced kernel took
+// 23.6 ms (74.0% of 8 TB/s), the same tokens as 128 launches of 8192 back to
+// back 22.5 ms (77.5%) -- each launch boundary being such a barrier.
+//
+// The barrier only paces; it never orders data (every token is independent),
+// so it waits a bounded time: a workgroup that has waited `spin_ticks` of the
+// device's constant-rate clock goes on regardless, and results never depend
+// on it.  It has two levels, since 256 atomic increments of one word queue
+// behind each other (a one-level barrier cost ~15 us an epoch): the
+// workgroups count in kPaceGroups group counters (workgroup b in group
+// b mod kPaceGroups), the last arrival of a group counts in the top counter
+// and waits there, then raises its group's release word, which the group's
+// other workgroups wait on.  All counts accumulate over the call's epochs; a
+// `depart` counter sees every workgroup past its last barrier, and the last
+// one to depart sets the slot back to zero for the slot's next call.  Each
+// call takes its own slot of a file-scope array (the host deals the slots
+// round robin per device), every word on its own 256-byte line.
+#ifndef ENGRAM_FWD_EPOCH_STEPS
+#define ENGRAM_FWD_EPOCH_STEPS 32
+#endif
+#ifndef ENGRAM_FWD_PACE_GROUPS
+#define ENGRAM_FWD_PACE_GROUPS 16
+#endif
+constexpr int kFwdEpochSteps = ENGRAM_FWD_EPOCH_STEPS;
+constexpr int kPaceGroups = ENGRAM_FWD_PACE_GROUPS;
+constexpr int kPaceLineWords = 64;                         // 256 bytes
+constexpr int kPaceSlotLines = 2 + 2 * kPaceGroups;        // top, depart, group arrive and release words
+constexpr int kPaceSlotWords = kPaceSlotLines * kPaceLineWords;
+constexpr int kPaceSlots = 16;
+static __device__ __align__(256) uint32_t pace_counters[kPaceSlots * kPaceSlotWords];
+
+__device__ __forceinline__ uint32_t pace_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void pace_wait(const uint32_t* p, uint32_t target, uint64_t spin_ticks) {
+  const uint64_t start = wall_clock64();
+  while (pace_load(p) < target && wall_clock64() - start < spin_ticks) __builtin_amdgcn_s_sleep(2);
+}
+
+template <bool kSave>
+__global__ void __launch_bounds__(kFwdThreads)
+engram_fwd_paced_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ kv,
+                        const float* __restrict__ weight, const uint8_t* __restrict__ mask,
+                        uint16_t* __restrict__ out, float* __restrict__ saved, int64_t n, uint32_t* slot,
+                        int64_t epochs, uint64_t spin_ticks) {
+  const int s = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  float w[kFwdVecs][kVec];
+  load_weight_slice(weight, w, s, lane);
+  const int64_t G = gridDim.x;
+  const int groups = G < kPaceGroups ? (int)G : kPaceGroups;
+  const int g = (int)(blockIdx.x % groups);
+  const uint32_t group_size = (uint32_t)((G - g + groups - 1) / groups);
+  uint32_t* top = slot;
+  uint32_t* depart = slot + kPaceLineWords;
+  uint32_t* arrive = slot + (2 + g) * kPaceLineWords;
+  uint32_t* release = slot + (2 + kPaceGroups + g) * kPaceLineWords;
+  for (int64_t e = 0; e < epochs; ++e) {
+    const int64_t t0 = e * kFwdEpochSteps * G + blockIdx.x;
+    for (int j = 0; j < kFwdEpochSteps; ++j) {
+      const int64_t t = t0 + j * G;
+      if (t < n) fwd_token<kSave>(x, kv, mask, out, saved, w, t, s, lane);
     }
-    if (m) {  // masked tokens never need the value
-#pragma unroll
-      for (int i = 0; i < kFwdVecs; ++i) vr[i] = load16(vs + (lane + 64 * i) * kVec);
-    }
-
-    float sxx = 0.f, skk = 0.f, sxwk = 0.f;
-#pragma unroll
-    for (int i = 0; i < kFwdVecs; ++i) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float x0 = bf_lo(xr[i][q]), x1 = bf_hi(xr[i][q]);
-        const float k0 = bf_lo(kr[i][q]), k1 = bf_hi(kr[i][q]);
-        sxx = fmaf(x0, x0, sxx);
-        sxx = fmaf(x1, x1, sxx);
-        skk = fmaf(k0, k0, skk);
-        skk = fmaf(k1, k1, skk);
-        sxwk = fmaf(x0 * w[i][2 * q], k0, sxwk);
-        sxwk = fmaf(x1 * w[i][2 * q + 1], k1, sxwk);
-      }
-    }
-    sxx = read_lane(wave_sum_to_lane63(sxx), 63);
-    skk = read_lane(wave_sum_to_lane63(skk), 63);
-    sxwk = read_lane(wave_sum_to_lane63(sxwk), 63);
-
-    const float rx = 1.0f / sqrtf(sxx / (float)kHidden + kEps);
-    const float rk = 1.0f / sqrtf(skk / (float)kHidden + kEps);
-    const float dot = (sxwk * rx) * rk;
-    const float mag = sqrtf(fmaxf(fabsf(dot), kClamp));
-    const float z = dot > 0.f ? mag : (dot < 0.f ? -mag : 0.f);
-    const float gate = 1.0f / (1.0f + expf(-z));
-
-    uint16_t* os = out + t * (kStreams * kHidden) + s * kHidden;
-#pragma unroll
-    for (int i = 0; i < kFwdVecs; ++i) {
-      u32x4 o = xr[i];
-      if (m) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float o0 = fmaf(gate, bf_lo(vr[i][q]), bf_lo(xr[i][q]));
-          const float o1 = fmaf(gate, bf_hi(vr[i][q]), bf_hi(xr[i][q]));
-          o[q] = pack_bf16x2(o0, o1);
+    if (e + 1 < epochs) {
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t done = (uint32_t)(e + 1);
+        const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before + 1 == done * group_size) {  // the group's last arrival
+          __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          pace_wait(top, done * (uint32_t)groups, spin_ticks);
+          __hip_atomic_fetch_max(release, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          pace_wait(release, done, spin_ticks);
         }
       }
-      store16_stream(os + (lane + 64 * i) * kVec, o);
+      __syncthreads();
     }
-    if (kSave && lane == 0) {
-      const f32x4 sv = {m ? gate : 0.f, dot, rx, rk};
-      *reinterpret_cast<f32x4*>(saved + t * (kStreams * 4) + 4 * s) = sv;
+  }
+  if (epochs > 1 && threadIdx.x == 0) {
+    const uint32_t before = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (before + 1 == (uint32_t)G) {  // every workgroup is past its last barrier
+      for (int l = 0; l < kPaceSlotLines; ++l)
+        __hip_atomic_store(slot + l * kPaceLineWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -125,6 +236,56 @@ hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const 
   void* args[] = {&xp, &kvp, &weight, &mask, &op, &saved, &n};
   const void* fn = saved ? reinterpret_cast<const void*>(&engram_fwd_kernel<true>)
                          : reinterpret_cast<const void*>(&engram_fwd_kernel<false>);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kFwdThreads), args, 0, stream);
+}
+
+namespace {
+struct PaceDevice {
+  std::atomic<uint32_t*> base{nullptr};
+  std::atomic<uint64_t> ticks_per_us{0};
+  std::atomic<uint32_t> next_slot{0};
+};
+PaceDevice g_pace[kMaxScratchDevices];
+std::mutex g_pace_mu;
+}  // namespace
+
+int64_t fwd_paced_epochs(int64_t n, int grid) {
+  const int64_t per_wg = (n + grid - 1) / grid;
+  return (per_wg + kFwdEpochSteps - 1) / kFwdEpochSteps;
+}
+
+hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
+                            float* saved, int64_t n, int grid, hipStream_t stream) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  PaceDevice& pd = g_pace[dev];
+  if (!pd.base.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lock(g_pace_mu);
+    if (!pd.base.load(std::memory_order_relaxed)) {
+      int khz = 0;
+      e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+      if (e != hipSuccess) return e;
+      if (khz <= 0) return hipErrorInvalidValue;
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(pace_counters));
+      if (e != hipSuccess) return e;
+      pd.ticks_per_us.store((uint64_t)khz / 1000 > 0 ? (uint64_t)khz / 1000 : 1, std::memory_order_relaxed);
+      pd.base.store(static_cast<uint32_t*>(p), std::memory_order_release);
+    }
+  }
+  uint32_t* slot = pd.base.load(std::memory_order_acquire) +
+                   (size_t)(pd.next_slot.fetch_add(1, std::memory_order_relaxed) % kPaceSlots) * kPaceSlotWords;
+  int64_t epochs = fwd_paced_epochs(n, grid);
+  // a workgroup gives up waiting after 200 us (an epoch itself takes ~180 us)
+  uint64_t spin_ticks = 200 * pd.ticks_per_us.load(std::memory_order_relaxed);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* kvp = static_cast<const uint16_t*>(kv);
+  uint16_t* op = static_cast<uint16_t*>(out);
+  void* args[] = {&xp, &kvp, &weight, &mask, &op, &saved, &n, &slot, &epochs, &spin_ticks};
+  const void* fn = saved ? reinterpret_cast<const void*>(&engram_fwd_paced_kernel<true>)
+                         : reinterpret_cast<const void*>(&engram_fwd_paced_kernel<false>);
   return hipLaunchKernel(fn, dim3(grid), dim3(kFwdThreads), args, 0, stream);
 }
 

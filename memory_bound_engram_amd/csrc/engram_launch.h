@@ -11,6 +11,13 @@ namespace engram {
 hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
                       float* saved, int64_t n, int grid, hipStream_t stream);
 
+// Enqueue the paced forward for long calls: `grid` workgroups, one per CU,
+// walking the tokens in epochs with a bounded-wait barrier between them; the
+// same per-token arithmetic as launch_fwd, so the same out and saved.
+hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
+                            float* saved, int64_t n, int grid, hipStream_t stream);
+int64_t fwd_paced_epochs(int64_t n, int grid);
+
 // Enqueue the backward main kernel (4 workgroups per partial row: N/64 rows,
 // or 64 above N = 4096 when 256 divides N) and the grad_weight reduction;
 // `partial` has room for N/64 rows of [4][5120] fp32 (written, then read
@@ -24,6 +31,9 @@ hipError_t launch_bwd(const void* x, const void* kv, const float* weight, const 
 // address for.
 constexpr int64_t kMaxBwdTokens = 8192;
 constexpr int kMaxScratchDevices = 64;
+
+// Calls longer than this many tokens take the paced forward.
+constexpr int64_t kFwdPacedMinTokens = 16384;
 
 // Device address, on the current device, of the library's own partial-row
 // array (room for kMaxBwdTokens tokens); taken once per device.

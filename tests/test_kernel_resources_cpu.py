@@ -57,7 +57,7 @@ def test_every_kernel_is_reported(resources):
     for src in SOURCES:
         assert resources[src], f"no kernels reported for {src}"
     names = " ".join(k for r in resources.values() for k in r)
-    for k in ("engram_fwd_kernel", "engram_bwd_main_kernel", "engram_bwd_reduce_kernel",
+    for k in ("engram_fwd_kernel", "engram_fwd_paced_kernel", "engram_bwd_main_kernel", "engram_bwd_reduce_kernel",
               "gateconv_fwd_kernel", "gateconv_bwd_conv_kernel", "gateconv_bwd_hk_kernel", "gateconv_reduce_kernel"):
         assert k in names, k
 
