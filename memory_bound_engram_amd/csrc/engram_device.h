@@ -89,4 +89,60 @@ __device__ __forceinline__ float read_lane(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// ---- pacing barrier: keeps the workgroups of a long kernel in step ----
+//
+// Workgroups that run a long loop drift apart, so that at any moment some of
+// them read while others write; kept in step, the chip reads a band of tokens,
+// then writes it, and HBM delivers more.  The barrier only paces -- no kernel
+// exchanges data through it -- so every wait is bounded (`spin_ticks` of the
+// device's constant-rate clock) and results never depend on it.  Two levels,
+// since 256 atomic increments of one word queue behind each other (a one-level
+// barrier cost ~15 us): the G workgroups count in kPaceGroups group counters
+// (workgroup b in group b mod kPaceGroups), the last arrival of a group counts
+// in the top counter and waits there, then raises its group's release word,
+// which the group's other workgroups wait on.  Counts accumulate over a call's
+// barriers; `depart` counts workgroups past their last barrier, and the last to
+// depart sets the slot back to zero for its next call.  A slot is a run of
+// 256-byte lines, one word used in each.  Called by one thread per workgroup.
+constexpr int kPaceGroups = 16;
+constexpr int kPaceLineWords = 64;                   // 256 bytes
+constexpr int kPaceSlotLines = 2 + 2 * kPaceGroups;  // top, depart, group arrive words, group release words
+constexpr int kPaceSlotWords = kPaceSlotLines * kPaceLineWords;
+
+__device__ __forceinline__ void pace_wait(const uint32_t* p, uint32_t target, uint64_t spin_ticks) {
+  const uint64_t start = wall_clock64();
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+         wall_clock64() - start < spin_ticks)
+    __builtin_amdgcn_s_sleep(2);
+}
+
+// The `done`-th barrier of the call (done = 1, 2, ...) for workgroup wg of G.
+__device__ __forceinline__ void pace_barrier(uint32_t* slot, uint32_t done, uint32_t wg, uint32_t G,
+                                             uint64_t spin_ticks) {
+  const uint32_t groups = G < (uint32_t)kPaceGroups ? G : (uint32_t)kPaceGroups;
+  const uint32_t g = wg % groups;
+  const uint32_t group_size = (G - g + groups - 1) / groups;
+  uint32_t* top = slot;
+  uint32_t* arrive = slot + (2 + g) * kPaceLineWords;
+  uint32_t* release = slot + (2 + kPaceGroups + g) * kPaceLineWords;
+  const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (before + 1 == done * group_size) {  // the group's last arrival
+    __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pace_wait(top, done * groups, spin_ticks);
+    __hip_atomic_fetch_max(release, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    pace_wait(release, done, spin_ticks);
+  }
+}
+
+// After a workgroup's last barrier of the call.
+__device__ __forceinline__ void pace_depart(uint32_t* slot, uint32_t G) {
+  uint32_t* depart = slot + kPaceLineWords;
+  const uint32_t before = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (before + 1 == G) {  // every workgroup is past its last barrier
+    for (int l = 0; l < kPaceSlotLines; ++l)
+      __hip_atomic_store(slot + l * kPaceLineWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace engram

@@ -135,49 +135,20 @@ engram_fwd_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ k
 //
 // A long call is walked in epochs: one workgroup per CU (all resident at
 // once), workgroup b taking tokens b + G i (G = grid size), and after every
-// kFwdEpochSteps of them the workgroups wait for each other at a soft barrier
-// before the next epoch.  Workgroups that run one long strided loop drift
-// apart, so that at any moment some of them read while others write; kept
-// together, the chip reads a band of tokens, then writes it.  Measured on
-// MI355X at N = 1,048,512 (one set of buffers): the unpaced kernel took
-// 23.6 ms (74.0% of 8 TB/s), the same tokens as 128 launches of 8192 back to
-// back 22.5 ms (77.5%) -- each launch boundary being such a barrier.
-//
-// The barrier only paces; it never orders data (every token is independent),
-// so it waits a bounded time: a workgroup that has waited `spin_ticks` of the
-// device's constant-rate clock goes on regardless, and results never depend
-// on it.  It has two levels, since 256 atomic increments of one word queue
-// behind each other (a one-level barrier cost ~15 us an epoch): the
-// workgroups count in kPaceGroups group counters (workgroup b in group
-// b mod kPaceGroups), the last arrival of a group counts in the top counter
-// and waits there, then raises its group's release word, which the group's
-// other workgroups wait on.  All counts accumulate over the call's epochs; a
-// `depart` counter sees every workgroup past its last barrier, and the last
-// one to depart sets the slot back to zero for the slot's next call.  Each
-// call takes its own slot of a file-scope array (the host deals the slots
-// round robin per device), every word on its own 256-byte line.
+// kFwdEpochSteps of them the workgroups meet at the pacing barrier
+// (engram_device.h) before the next epoch.  Measured on MI355X at
+// N = 1,048,512 on one set of buffers: the unpaced kernel took 23.6-24.1 ms
+// (72-74% of 8 TB/s), the same tokens as 128 launches of 8192 back to back
+// 22.4-22.5 ms, this kernel 22.3-22.4 ms (78%); epochs of 16 tokens were
+// slower (22.8 ms: more barriers), of 64 the same as 32; 8 or 32 barrier
+// groups the same as 16.  Each call takes its own slot of a file-scope
+// counter array, dealt round robin per device by pace_slot().
 #ifndef ENGRAM_FWD_EPOCH_STEPS
 #define ENGRAM_FWD_EPOCH_STEPS 32
 #endif
-#ifndef ENGRAM_FWD_PACE_GROUPS
-#define ENGRAM_FWD_PACE_GROUPS 16
-#endif
 constexpr int kFwdEpochSteps = ENGRAM_FWD_EPOCH_STEPS;
-constexpr int kPaceGroups = ENGRAM_FWD_PACE_GROUPS;
-constexpr int kPaceLineWords = 64;                         // 256 bytes
-constexpr int kPaceSlotLines = 2 + 2 * kPaceGroups;        // top, depart, group arrive and release words
-constexpr int kPaceSlotWords = kPaceSlotLines * kPaceLineWords;
 constexpr int kPaceSlots = 16;
 static __device__ __align__(256) uint32_t pace_counters[kPaceSlots * kPaceSlotWords];
-
-__device__ __forceinline__ uint32_t pace_load(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void pace_wait(const uint32_t* p, uint32_t target, uint64_t spin_ticks) {
-  const uint64_t start = wall_clock64();
-  while (pace_load(p) < target && wall_clock64() - start < spin_ticks) __builtin_amdgcn_s_sleep(2);
-}
 
 template <bool kSave>
 __global__ void __launch_bounds__(kFwdThreads)
@@ -190,13 +161,6 @@ engram_fwd_paced_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
   float w[kFwdVecs][kVec];
   load_weight_slice(weight, w, s, lane);
   const int64_t G = gridDim.x;
-  const int groups = G < kPaceGroups ? (int)G : kPaceGroups;
-  const int g = (int)(blockIdx.x % groups);
-  const uint32_t group_size = (uint32_t)((G - g + groups - 1) / groups);
-  uint32_t* top = slot;
-  uint32_t* depart = slot + kPaceLineWords;
-  uint32_t* arrive = slot + (2 + g) * kPaceLineWords;
-  uint32_t* release = slot + (2 + kPaceGroups + g) * kPaceLineWords;
   for (int64_t e = 0; e < epochs; ++e) {
     const int64_t t0 = e * kFwdEpochSteps * G + blockIdx.x;
     for (int j = 0; j < kFwdEpochSteps; ++j) {
@@ -205,27 +169,11 @@ engram_fwd_paced_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
     }
     if (e + 1 < epochs) {
       __syncthreads();
-      if (threadIdx.x == 0) {
-        const uint32_t done = (uint32_t)(e + 1);
-        const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (before + 1 == done * group_size) {  // the group's last arrival
-          __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          pace_wait(top, done * (uint32_t)groups, spin_ticks);
-          __hip_atomic_fetch_max(release, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          pace_wait(release, done, spin_ticks);
-        }
-      }
+      if (threadIdx.x == 0) pace_barrier(slot, (uint32_t)(e + 1), blockIdx.x, (uint32_t)G, spin_ticks);
       __syncthreads();
     }
   }
-  if (epochs > 1 && threadIdx.x == 0) {
-    const uint32_t before = __hip_atomic_fetch_add(depart, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (before + 1 == (uint32_t)G) {  // every workgroup is past its last barrier
-      for (int l = 0; l < kPaceSlotLines; ++l)
-        __hip_atomic_store(slot + l * kPaceLineWords, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  if (epochs > 1 && threadIdx.x == 0) pace_depart(slot, (uint32_t)G);
 }
 
 hipError_t launch_fwd(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
@@ -249,13 +197,7 @@ PaceDevice g_pace[kMaxScratchDevices];
 std::mutex g_pace_mu;
 }  // namespace
 
-int64_t fwd_paced_epochs(int64_t n, int grid) {
-  const int64_t per_wg = (n + grid - 1) / grid;
-  return (per_wg + kFwdEpochSteps - 1) / kFwdEpochSteps;
-}
-
-hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
-                            float* saved, int64_t n, int grid, hipStream_t stream) {
+hipError_t pace_slot(uint32_t** slot, uint64_t* ticks_per_us) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -269,17 +211,32 @@ hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, 
       if (e != hipSuccess) return e;
       if (khz <= 0) return hipErrorInvalidValue;
       void* p = nullptr;
-      e = hipGetSymbolAddress(&p, HIP_SYMBOL(pace_counters));
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(pace_counters));  // this device's copy of the array
       if (e != hipSuccess) return e;
       pd.ticks_per_us.store((uint64_t)khz / 1000 > 0 ? (uint64_t)khz / 1000 : 1, std::memory_order_relaxed);
       pd.base.store(static_cast<uint32_t*>(p), std::memory_order_release);
     }
   }
-  uint32_t* slot = pd.base.load(std::memory_order_acquire) +
-                   (size_t)(pd.next_slot.fetch_add(1, std::memory_order_relaxed) % kPaceSlots) * kPaceSlotWords;
+  *slot = pd.base.load(std::memory_order_acquire) +
+          (size_t)(pd.next_slot.fetch_add(1, std::memory_order_relaxed) % kPaceSlots) * kPaceSlotWords;
+  *ticks_per_us = pd.ticks_per_us.load(std::memory_order_relaxed);
+  return hipSuccess;
+}
+
+int64_t fwd_paced_epochs(int64_t n, int grid) {
+  const int64_t per_wg = (n + grid - 1) / grid;
+  return (per_wg + kFwdEpochSteps - 1) / kFwdEpochSteps;
+}
+
+hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, const uint8_t* mask, void* out,
+                            float* saved, int64_t n, int grid, hipStream_t stream) {
+  uint32_t* slot = nullptr;
+  uint64_t ticks_per_us = 0;
+  const hipError_t e = pace_slot(&slot, &ticks_per_us);
+  if (e != hipSuccess) return e;
   int64_t epochs = fwd_paced_epochs(n, grid);
   // a workgroup gives up waiting after 200 us (an epoch itself takes ~180 us)
-  uint64_t spin_ticks = 200 * pd.ticks_per_us.load(std::memory_order_relaxed);
+  uint64_t spin_ticks = 200 * ticks_per_us;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* kvp = static_cast<const uint16_t*>(kv);
   uint16_t* op = static_cast<uint16_t*>(out);

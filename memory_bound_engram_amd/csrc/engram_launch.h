@@ -18,6 +18,10 @@ hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, 
                             float* saved, int64_t n, int grid, hipStream_t stream);
 int64_t fwd_paced_epochs(int64_t n, int grid);
 
+// A slot of the pacing counters (zero between calls) for the next call on the
+// current device, dealt round robin, and the device clock's ticks per us.
+hipError_t pace_slot(uint32_t** slot, uint64_t* ticks_per_us);
+
 // Enqueue the backward main kernel (4 workgroups per partial row: N/64 rows,
 // or 64 above N = 4096 when 256 divides N) and the grad_weight reduction;
 // `partial` has room for N/64 rows of [4][5120] fp32 (written, then read
