@@ -40,11 +40,13 @@
  *     each other; outputs and workspace must not overlap any input or each
  *     other (saved-state paragraph).
  *   - The library holds no state between calls beyond per-device caches of
- *     fixed facts (the CU count, the address of its own scratch array), and
- *     is thread-safe; calls on different streams are independent, except
+ *     fixed facts (the CU count, the addresses of its own device arrays) and
+ *     the round-robin position of the forward's pacing slots, and is
+ *     thread-safe; calls on different streams are independent, except
  *     engram_gate_bwd_noalloc calls on one GPU, which share that GPU's
  *     scratch array.  Results are bitwise reproducible for identical inputs
- *     (fixed reduction orders, no atomics).
+ *     (fixed reduction orders; the only atomics are the forward's pacing
+ *     counters, which no result depends on).
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H
@@ -97,7 +99,9 @@ typedef enum {
  * robin, each set back to zero by the call that used it).  They only pace the
  * kernel: results never depend on them, and every wait on them is bounded, so
  * more than 16 such calls in flight at once on one GPU (sharing a slot) can
- * run slower but not differently or forever.
+ * run slower but not differently or forever.  The environment variable
+ * ENGRAM_PACE_WAIT_US (read at every call; 0..1000000, default 200) bounds
+ * one wait in microseconds; 0 turns the pacing off.
  */
 engram_status engram_gate_fwd(const void *x, const void *kv, const float *weight, const uint8_t *mask,
                               void *out, float *saved, int64_t N, void *stream);

@@ -25,6 +25,7 @@
 #include "engram_launch.h"
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 namespace engram {
@@ -223,6 +224,19 @@ hipError_t pace_slot(uint32_t** slot, uint64_t* ticks_per_us) {
   return hipSuccess;
 }
 
+// Longest wait at a pacing barrier, in microseconds: ENGRAM_PACE_WAIT_US if
+// set to a number in 0..1000000 (0: no workgroup waits, i.e. no pacing), else
+// 200 (an epoch itself takes ~180 us at full speed).  Read at every call.
+uint64_t pace_wait_us() {
+  const char* v = std::getenv("ENGRAM_PACE_WAIT_US");
+  if (v && *v) {
+    char* end = nullptr;
+    const long long us = std::strtoll(v, &end, 10);
+    if (end && *end == '\0' && us >= 0 && us <= 1000000) return (uint64_t)us;
+  }
+  return 200;
+}
+
 int64_t fwd_paced_epochs(int64_t n, int grid) {
   const int64_t per_wg = (n + grid - 1) / grid;
   return (per_wg + kFwdEpochSteps - 1) / kFwdEpochSteps;
@@ -235,8 +249,7 @@ hipError_t launch_fwd_paced(const void* x, const void* kv, const float* weight, 
   const hipError_t e = pace_slot(&slot, &ticks_per_us);
   if (e != hipSuccess) return e;
   int64_t epochs = fwd_paced_epochs(n, grid);
-  // a workgroup gives up waiting after 200 us (an epoch itself takes ~180 us)
-  uint64_t spin_ticks = 200 * ticks_per_us;
+  uint64_t spin_ticks = pace_wait_us() * ticks_per_us;
   const uint16_t* xp = static_cast<const uint16_t*>(x);
   const uint16_t* kvp = static_cast<const uint16_t*>(kv);
   uint16_t* op = static_cast<uint16_t*>(out);
