@@ -106,14 +106,24 @@ __device__ __forceinline__ float read_lane(float v, int lane) {
 // 256-byte lines, one word used in each.  Called by one thread per workgroup.
 constexpr int kPaceGroups = 16;
 constexpr int kPaceLineWords = 64;                   // 256 bytes
-constexpr int kPaceSlotLines = 2 + 2 * kPaceGroups;  // top, depart, group arrive words, group release words
+constexpr int kPaceSlotLines = 3 + 2 * kPaceGroups;  // top, depart, abandon, group arrive words, group release words
 constexpr int kPaceSlotWords = kPaceSlotLines * kPaceLineWords;
 
-__device__ __forceinline__ void pace_wait(const uint32_t* p, uint32_t target, uint64_t spin_ticks) {
+// Wait until *p >= target.  A wait that runs out of time marks the call's
+// slot abandoned, and every later wait of the call sees that and returns at
+// once: a call whose workgroups cannot all be resident (other kernels hold
+// CUs) pays the bound once, then runs unpaced.
+__device__ __forceinline__ void pace_wait(uint32_t* slot, const uint32_t* p, uint32_t target, uint64_t spin_ticks) {
+  uint32_t* abandon = slot + 2 * kPaceLineWords;
   const uint64_t start = wall_clock64();
-  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
-         wall_clock64() - start < spin_ticks)
+  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    if (__hip_atomic_load(abandon, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+    if (wall_clock64() - start >= spin_ticks) {
+      __hip_atomic_store(abandon, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
     __builtin_amdgcn_s_sleep(2);
+  }
 }
 
 // The `done`-th barrier of the call (done = 1, 2, ...) for workgroup wg of G.
@@ -123,15 +133,15 @@ __device__ __forceinline__ void pace_barrier(uint32_t* slot, uint32_t done, uint
   const uint32_t g = wg % groups;
   const uint32_t group_size = (G - g + groups - 1) / groups;
   uint32_t* top = slot;
-  uint32_t* arrive = slot + (2 + g) * kPaceLineWords;
-  uint32_t* release = slot + (2 + kPaceGroups + g) * kPaceLineWords;
+  uint32_t* arrive = slot + (3 + g) * kPaceLineWords;
+  uint32_t* release = slot + (3 + kPaceGroups + g) * kPaceLineWords;
   const uint32_t before = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (before + 1 == done * group_size) {  // the group's last arrival
     __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pace_wait(top, done * groups, spin_ticks);
+    pace_wait(slot, top, done * groups, spin_ticks);
     __hip_atomic_fetch_max(release, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    pace_wait(release, done, spin_ticks);
+    pace_wait(slot, release, done, spin_ticks);
   }
 }
 
