@@ -99,7 +99,9 @@ typedef enum {
  * robin, each set back to zero by the call that used it).  They only pace the
  * kernel: results never depend on them, and every wait on them is bounded, so
  * more than 16 such calls in flight at once on one GPU (sharing a slot) can
- * run slower but not differently or forever.  The environment variable
+ * run slower but not differently or forever; a call whose wait runs out
+ * (its workgroups not all resident, e.g. beside another kernel) stops pacing
+ * for the rest of that call.  The environment variable
  * ENGRAM_PACE_WAIT_US (read at every call; 0..1000000, default 200) bounds
  * one wait in microseconds; 0 turns the pacing off.
  */

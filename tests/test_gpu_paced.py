@@ -185,7 +185,8 @@ def test_paced_graph_replays(gpu):
 
 
 def test_paced_results_do_not_depend_on_the_barrier(gpu, monkeypatch):
-    """ENGRAM_PACE_WAIT_US=0: every wait at the pacing barrier gives up at
+    """ENGRAM_PACE_WAIT_US=0: the first wait at the pacing barrier runs out at
+    once and marks the call's slot abandoned, so every later wait returns at
     once (the kernel still counts through every barrier and resets its slot).
     The results stay bit-identical to the unpaced path, and a normally paced
     call right after still finds its slot clean (same results, no slower than
